@@ -1,0 +1,229 @@
+"""Seeded synthetic inputs for paged attention.
+
+This module builds tensors only: query, paged K/V caches, block tables and
+sequence lengths, at the shapes of the decode and prefill workloads the pages
+measure.  It contains no attention arithmetic, so both the CPU oracle and the
+HIP path can be fed from it without sharing any of the method's code.
+
+Recipe (the same for every workload):
+
+* ``torch.Generator(device).manual_seed(seed)`` drives the page permutation,
+  then ``q``, ``k_cache`` and ``v_cache`` as standard normals drawn in float32
+  and rounded to the workload's dtype; the oracle reads the rounded values.
+  Ragged lengths come from a CPU generator with the same seed, so the layout
+  is the same whatever the device.
+* Physical pages are assigned by a seeded random permutation, so logical and
+  physical order differ.
+* Block-table slots a sequence does not use hold the unmapped id
+  ``0x7FFFFFFF``; pages no sequence references, and the token slots of a last
+  page past a sequence's length, are filled with NaN so that any stray read
+  shows up in the result.
+
+Workloads (``WORKLOADS``):
+
+``tiny_f32``        B=2, Hq=4, Hkv=2, D=64, page 16, lengths {37, 200}, 16
+                    slots per row over 30 physical pages, splits {1, 3}.
+``prefill_f16``     one batch-head, Sq = L = 1024, D=32, page 32 (1024
+                    elements), 32 shuffled pages, causal, splits {1, 4}.
+``ragged_bf16``     B=8, Hq=32, Hkv=8, D=128, page 16, lengths uniform in
+                    [17, 1000], table 63 slots wide read through a view whose
+                    tail holds the unmapped id, cache page count overstated
+                    (65,538), splits 1..8.
+``llama3_8b_decode`` B=256, Hq=32, Hkv=8, D=128, page 16, L=4096, K and V
+                    caches of exactly 2 GiB (65,536 pages of 32 KiB), table a
+                    seeded permutation of all pages, splits auto.
+``qwen3_235b_decode`` B=256, Hq=64, Hkv=4, D=128, page 16, L=8192, 2 GiB per
+                    cache (131,072 pages of 16 KiB); variant ``straddle`` with
+                    131,328 pages (2 GiB + 4 MiB) so used pages lie on both
+                    sides of byte offset 2^31.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+UNMAPPED_PAGE = 0x7FFFFFFF
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    dtype: str
+    batch: int
+    seq_q: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    causal: bool
+    splits: tuple
+    seed: int
+    description: str
+
+
+WORKLOADS = {
+    "tiny_f32": WorkloadSpec("tiny_f32", "f32", 2, 1, 4, 2, 64, 16, False, (1, 3), 0,
+                             "tiny paged GQA decode f32 B=2 Hq=4 Hkv=2 D=64 page16 L={37,200}"),
+    "prefill_f16": WorkloadSpec("prefill_f16", "f16", 1, 1024, 1, 1, 32, 32, True, (1, 4), 1,
+                                "paged causal prefill f16 Sq=L=1024 H=1 D=32 page32, 32 pages"),
+    "ragged_bf16": WorkloadSpec("ragged_bf16", "bf16", 8, 1, 32, 8, 128, 16, False,
+                                tuple(range(1, 9)), 2,
+                                "ragged paged decode bf16 B=8 Hq=32 Hkv=8 D=128 page16 L~U[17,1000]"),
+    "llama3_8b_decode": WorkloadSpec("llama3_8b_decode", "bf16", 256, 1, 32, 8, 128, 16, False,
+                                     (0,), 3,
+                                     "Llama-3-8B decode bf16 B=256 Hq=32 Hkv=8 D=128 page16 Skv=4096"),
+    "qwen3_235b_decode": WorkloadSpec("qwen3_235b_decode", "bf16", 256, 1, 64, 4, 128, 16, False,
+                                      (0,), 4,
+                                      "Qwen3-235B-A22B decode bf16 B=256 Hq=64 Hkv=4 D=128 page16 Skv=8192"),
+}
+
+WORKLOAD_ORDER = ["tiny_f32", "prefill_f16", "ragged_bf16", "llama3_8b_decode", "qwen3_235b_decode"]
+
+
+@dataclass
+class PagedInputs:
+    """One batch of paged-attention inputs (all tensors on ``device``)."""
+
+    spec: WorkloadSpec
+    q: torch.Tensor              # [B, Sq, Hq, D]
+    k_cache: torch.Tensor        # [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor        # [num_pages, page_size, Hkv, D]
+    block_table: torch.Tensor    # int32 [B, W], possibly a strided view
+    seq_lens: torch.Tensor       # int32 [B]
+    scale: float
+    causal: bool
+    num_pages_arg: int           # page count handed to the library (may be overstated)
+    seq_lens_host: List[int] = field(default_factory=list)
+    table_host: Optional[torch.Tensor] = None   # CPU int32 copy of block_table
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+
+def _normal(gen, shape, dtype, device):
+    return torch.randn(shape, generator=gen, dtype=torch.float32, device=device).to(dtype)
+
+
+def _poison_unused(cache: torch.Tensor, used_pages: torch.Tensor, lens: List[int],
+                   table: torch.Tensor, page_size: int):
+    """NaN into unreferenced pages and into the slots past each sequence's end."""
+    if not cache.dtype.is_floating_point:
+        return
+    mask = torch.ones(cache.shape[0], dtype=torch.bool, device=cache.device)
+    mask[used_pages.long()] = False
+    cache[mask] = float("nan")
+    for b, seq_len in enumerate(lens):
+        n = -(-seq_len // page_size)
+        tail = n * page_size - seq_len
+        if n and tail:
+            cache[int(table[b, n - 1])][page_size - tail:] = float("nan")
+
+
+def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: Optional[str] = None,
+                  seq_lens: Optional[List[int]] = None, batch: Optional[int] = None,
+                  table_stride: Optional[int] = None) -> PagedInputs:
+    """Build the named workload on ``device``.
+
+    ``seed`` defaults to the workload's own.  ``variant`` selects a variant
+    (``"straddle"`` for the Qwen3 shape; ``"contiguous"`` for an identity page
+    order on the two large decode shapes).  ``seq_lens``/``batch`` override the
+    lengths (tests use this for edge cases on the small workloads).
+    ``table_stride`` reads the block table through a row stride larger than
+    its width.
+    """
+    spec = WORKLOADS[name]
+    seed = spec.seed if seed is None else seed
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dtype = DTYPES[spec.dtype]
+    ps, hkv, d, hq = spec.page_size, spec.num_kv_heads, spec.head_dim, spec.num_q_heads
+
+    if name == "tiny_f32":
+        lens = list(seq_lens) if seq_lens is not None else [37, 200]
+        width, phys = 16, 30
+    elif name == "prefill_f16":
+        lens = list(seq_lens) if seq_lens is not None else [1024]
+        width, phys = 32, 32
+    elif name == "ragged_bf16":
+        b = batch if batch is not None else spec.batch
+        width = 63
+        if seq_lens is not None:
+            lens = list(seq_lens)
+        else:
+            lens = torch.randint(17, 1001, (b,), generator=torch.Generator().manual_seed(seed)).tolist()
+        phys = sum(-(-x // ps) for x in lens) + 8   # a little slack, poisoned
+    elif name == "llama3_8b_decode":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [4096] * b
+        width, phys = 256, 65536 if batch is None else max(1, b * 256)
+    elif name == "qwen3_235b_decode":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [8192] * b
+        width = 512
+        phys = 131328 if variant == "straddle" else (131072 if batch is None else max(1, b * 512))
+    else:
+        raise KeyError(name)
+
+    bsz = len(lens)
+    n_per = [-(-x // ps) for x in lens]
+    if max(n_per, default=0) > width:
+        raise ValueError("sequence longer than the block table allows")
+    total_used = sum(n_per)
+    if total_used > phys:
+        raise ValueError("not enough physical pages")
+
+    # --- page assignment -------------------------------------------------------
+    if variant == "contiguous":
+        perm = torch.arange(phys, dtype=torch.int64, device=device)
+    else:
+        perm = torch.randperm(phys, generator=gen, device=device)
+    stride = width if table_stride is None else int(table_stride)
+    if stride < width:
+        raise ValueError("table stride smaller than its width")
+    # storage: rows of `stride` slots plus a 64-entry tail, all unmapped first
+    storage = torch.full((bsz * stride + 64,), UNMAPPED_PAGE, dtype=torch.int32, device=device)
+    used = perm[:total_used].to(torch.int32)
+    rows = storage[: bsz * stride].view(bsz, stride)
+    pos = 0
+    for b, n in enumerate(n_per):
+        rows[b, :n] = used[pos:pos + n]
+        pos += n
+    table = rows[:, :width]   # view; row stride `stride`, the storage tail is unmapped
+
+    # --- values -----------------------------------------------------------------
+    q = _normal(gen, (bsz, spec.seq_q, hq, d), dtype, device)
+    k_cache = _normal(gen, (phys, ps, hkv, d), dtype, device)
+    v_cache = _normal(gen, (phys, ps, hkv, d), dtype, device)
+    if name in ("tiny_f32", "ragged_bf16", "prefill_f16"):
+        _poison_unused(k_cache, used, lens, table, ps)
+        _poison_unused(v_cache, used, lens, table, ps)
+
+    num_pages_arg = 65538 if name == "ragged_bf16" else phys
+    seq_lens_t = torch.tensor(lens, dtype=torch.int32, device=device)
+    inputs = PagedInputs(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache, block_table=table,
+                         seq_lens=seq_lens_t, scale=1.0 / math.sqrt(d), causal=spec.causal,
+                         num_pages_arg=num_pages_arg, seq_lens_host=list(lens),
+                         table_host=table.cpu())
+    inputs.notes["true_num_pages"] = phys
+    inputs.notes["table_storage"] = storage
+    inputs.notes["variant"] = variant
+    if variant == "straddle":
+        page_bytes = ps * hkv * d * k_cache.element_size()
+        inputs.notes["max_used_page_start_bytes"] = int(used.max()) * page_bytes
+    return inputs
+
+
+def kv_bytes(inputs: PagedInputs) -> int:
+    """Algorithmic K+V bytes one decode step reads: every element of the first
+    L tokens of each sequence, once, for K and for V."""
+    spec = inputs.spec
+    per_token = spec.num_kv_heads * spec.head_dim * inputs.k_cache.element_size()
+    return 2 * per_token * sum(inputs.seq_lens_host)

@@ -1,0 +1,101 @@
+"""Writes the closed-form fixtures in this folder.
+
+The pages print no worked numeric example, so each fixture is a case built so
+that its answer is a closed form (derivation stored beside the numbers).  The
+values here come from ``math`` only; nothing is computed by the oracle or by
+the HIP path.  Run ``python tests/golden/make_golden.py`` to rewrite them.
+"""
+
+import json
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NEG_INF = "-inf"   # JSON has no infinity; readers map this string to -inf
+
+FIXTURES = {
+    "hand_case": {
+        "description": "Hand-worked paged attention case. One sequence of two tokens stored in two "
+                       "one-token pages in swapped physical order.",
+        "citation": "Definition of the result: softmax attention over the logical-order cache "
+                    "(rocMLIR 'Paged Attention: rocmlir-gen changes', Technical Details, CPU "
+                    "Validation); the paged input is a view of that cache (rocMLIR 'Paged "
+                    "Attention: migraphx & highlevel pipeline changes', note on rock.deref). The "
+                    "pages print no worked example; this case is constructed so the answer is a "
+                    "closed form.",
+        "derivation": "scores: q.k0 = 0, q.k1 = ln 3; weights e^0 = 1 and e^(ln 3) = 3 sum to 4; "
+                      "out = (1*v0 + 3*v1)/4 = (0.25, 0.75); lse = ln(1 + 3) = ln 4.",
+        "dtype": "f32", "page_size": 1, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": False,
+        "q": [[[[1.0, 0.0]]]],
+        "k_cache_pages": [[[[math.log(3.0), 0.0]]], [[[0.0, 0.0]]]],
+        "v_cache_pages": [[[[0.0, 1.0]]], [[[1.0, 0.0]]]],
+        "block_table": [[1, 0]],
+        "seq_lens": [2],
+        "expected_out": [[[[0.25, 0.75]]]],
+        "expected_lse": [[[math.log(4.0)]]],
+    },
+    "split_closed_form": {
+        "description": "Split-KV closed form: L=3 one-token pages, S=2 splits, q=0 so every valid "
+                       "score is 0 and each split's output is the mean of its V rows.",
+        "citation": "Split ranges by ceiling division with the end clamped, per-split normalised "
+                    "output and LSE, and the LSE combine: rocMLIR 'Fix split-kv attention masking "
+                    "and sweep RMS', Technical Details (non-causal split-KV iteration math; "
+                    "scaleFinalOutput; host reference f32 combine).",
+        "derivation": "P = ceil(3/2) = 2: split 0 holds tokens 0,1 -> out (v0+v1)/2 = (0.5, 0.5), "
+                      "lse ln 2; split 1 holds token 2 -> out v2 = (2, 2), lse ln 1 = 0. Combine: "
+                      "weights 2 and 1 (exp of lse minus max, times 2) -> out (2*(0.5,0.5) + "
+                      "1*(2,2))/3 = (1, 1), lse ln 2 + ln(1 + 1/2) = ln 3.",
+        "dtype": "f32", "page_size": 1, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": False, "num_splits": 2,
+        "q": [[[[0.0, 0.0]]]],
+        "k_cache_pages": [[[[0.3, -1.0]]], [[[2.0, 0.5]]], [[[-0.7, 0.1]]]],
+        "v_cache_pages": [[[[1.0, 0.0]]], [[[0.0, 1.0]]], [[[2.0, 2.0]]]],
+        "block_table": [[0, 1, 2]],
+        "seq_lens": [3],
+        "expected_part_out": [[[[[0.5, 0.5], [2.0, 2.0]]]]],
+        "expected_part_lse": [[[[math.log(2.0), 0.0]]]],
+        "expected_out": [[[[1.0, 1.0]]]],
+        "expected_lse": [[[math.log(3.0)]]],
+    },
+    "causal_masked_split": {
+        "description": "Causal prefill with fully masked splits: Sq = L = 4 one-token pages, S = 2, "
+                       "q = 0. Rows 0 and 1 see no key of split 1, which must give (0, -inf) and "
+                       "not NaN.",
+        "citation": "Fully masked partitions contribute zero instead of NaN (-inf - (-inf) guard) "
+                    "and a zero row sum stores 0 (scaleFinalOutput 0/0 guard); causal validity per "
+                    "query row from its effective key length: rocMLIR 'Fix split-kv attention "
+                    "masking and sweep RMS', Motivation and Technical Details.",
+        "derivation": "Row i sees keys 0..i. P = ceil(4/2) = 2, split 0 = tokens 0,1, split 1 = "
+                      "tokens 2,3. V rows v0=(1,0), v1=(0,1), v2=(2,2), v3=(4,0). Row 0: split0 "
+                      "{0} -> (1,0), 0; split1 empty -> (0,0), -inf; combined (1,0), 0. Row 1: "
+                      "split0 {0,1} -> (0.5,0.5), ln2; split1 empty; combined (0.5,0.5), ln2. "
+                      "Row 2: split0 (0.5,0.5), ln2; split1 {2} -> (2,2), 0; combined (1,1), ln3. "
+                      "Row 3: split0 (0.5,0.5), ln2; split1 {2,3} -> (3,1), ln2; combined "
+                      "(7/4, 3/4), ln4.",
+        "dtype": "f32", "page_size": 1, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": True, "num_splits": 2,
+        "q": [[[[0.0, 0.0]], [[0.0, 0.0]], [[0.0, 0.0]], [[0.0, 0.0]]]],
+        "k_cache_pages": [[[[0.5, 0.5]]], [[[-1.0, 2.0]]], [[[0.25, 0.0]]], [[[3.0, -3.0]]]],
+        "v_cache_pages": [[[[1.0, 0.0]]], [[[0.0, 1.0]]], [[[2.0, 2.0]]], [[[4.0, 0.0]]]],
+        "block_table": [[0, 1, 2, 3]],
+        "seq_lens": [4],
+        "expected_part_out": [[[[[1.0, 0.0], [0.0, 0.0]]], [[[0.5, 0.5], [0.0, 0.0]]],
+                               [[[0.5, 0.5], [2.0, 2.0]]], [[[0.5, 0.5], [3.0, 1.0]]]]],
+        "expected_part_lse": [[[[0.0, NEG_INF]], [[math.log(2.0), NEG_INF]],
+                               [[math.log(2.0), 0.0]], [[math.log(2.0), math.log(2.0)]]]],
+        "expected_out": [[[[1.0, 0.0]], [[0.5, 0.5]], [[1.0, 1.0]], [[1.75, 0.75]]]],
+        "expected_lse": [[[0.0], [math.log(2.0)], [math.log(3.0)], [math.log(4.0)]]],
+    },
+}
+
+
+def main():
+    for name, obj in FIXTURES.items():
+        with open(os.path.join(HERE, name + ".json"), "w") as f:
+            json.dump(obj, f, indent=1)
+            f.write("\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,328 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each ``check_*`` function raises ``AssertionError`` when the oracle disagrees
+with an independent source: a closed-form fixture under ``tests/golden``, a
+pure-Python brute force, a closed form (``q = 0`` makes every valid score 0),
+torch's float64 scaled-dot-product attention on the unpaged special case, or
+an invariant (page shuffle, split equivalence, all-ones V).  The mutation
+tests plant mistakes in the oracle and require at least one check to fail.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.paged_attention as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+UNMAPPED = 0x7FFFFFFF
+
+
+def _to_float(x):
+    if isinstance(x, list):
+        return [_to_float(v) for v in x]
+    if x == "-inf":
+        return -math.inf
+    return float(x)
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name + ".json")) as f:
+        raw = json.load(f)
+    g = dict(raw)
+    for key in ("q", "k_cache_pages", "v_cache_pages", "expected_out", "expected_lse",
+                "expected_part_out", "expected_part_lse"):
+        if key in raw:
+            g[key] = np.array(_to_float(raw[key]), dtype=np.float64)
+    g["block_table"] = np.array(raw["block_table"], dtype=np.int64)
+    g["seq_lens"] = np.array(raw["seq_lens"], dtype=np.int64)
+    return g
+
+
+def _close(a, b, tol=1e-12):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    assert not np.isnan(a).any(), "NaN in oracle output"
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(same_inf, 0.0, np.abs(a - b))
+    assert (diff <= tol).all(), f"max diff {np.nanmax(diff)}"
+
+
+# ----------------------------------------------------------------------------- fixtures
+def check_golden_hand():
+    g = load_golden("hand_case")
+    out, lse = O.attention(g["q"], g["k_cache_pages"], g["v_cache_pages"], g["block_table"],
+                           g["seq_lens"], g["scale"], g["causal"])
+    _close(out, g["expected_out"])
+    _close(lse, g["expected_lse"])
+
+
+def check_golden_split(name="split_closed_form"):
+    g = load_golden(name)
+    args = (g["q"], g["k_cache_pages"], g["v_cache_pages"], g["block_table"], g["seq_lens"],
+            g["scale"], g["causal"])
+    po, pl = O.split_partials(*args, g["num_splits"])
+    _close(po, g["expected_part_out"])
+    _close(pl, g["expected_part_lse"])
+    out, lse = O.combine(po, pl)
+    _close(out, g["expected_out"])
+    _close(lse, g["expected_lse"])
+    out2, lse2 = O.attention(*args)
+    _close(out2, g["expected_out"])
+    _close(lse2, g["expected_lse"])
+
+
+def check_golden_causal():
+    check_golden_split("causal_masked_split")
+
+
+# ----------------------------------------------------------------------------- problems
+def random_problem(rng, batch=3, seq_q=1, hq=4, hkv=2, d=3, dv=None, ps=2, lens=None,
+                   width=None, extra_pages=3, poison=True):
+    """Small random paged problem in NumPy (pages shuffled, unused slots unmapped,
+    unreferenced pages and in-page tails NaN)."""
+    dv = d if dv is None else dv
+    if lens is None:
+        lens = [int(x) for x in rng.integers(0, 11, size=batch)]
+    n_per = [-(-x // ps) for x in lens]
+    width = max(max(n_per, default=0), 1) if width is None else width
+    used = sum(n_per)
+    phys = used + extra_pages
+    perm = rng.permutation(phys)
+    table = np.full((len(lens), width), UNMAPPED, dtype=np.int64)
+    pos = 0
+    for b, n in enumerate(n_per):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    k_cache = rng.standard_normal((phys, ps, hkv, d))
+    v_cache = rng.standard_normal((phys, ps, hkv, dv))
+    if poison:
+        unused = perm[used:]
+        k_cache[unused] = np.nan
+        v_cache[unused] = np.nan
+        for b, (x, n) in enumerate(zip(lens, n_per)):
+            tail = n * ps - x
+            if n and tail:
+                k_cache[table[b, n - 1], ps - tail:] = np.nan
+                v_cache[table[b, n - 1], ps - tail:] = np.nan
+    q = rng.standard_normal((len(lens), seq_q, hq, d))
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, block_table=table,
+                seq_lens=np.array(lens, dtype=np.int64), scale=1.0 / math.sqrt(d))
+
+
+def brute_force(q, k_cache, v_cache, block_table, seq_lens, scale, causal):
+    """Pure-Python attention: one key at a time, straight from the page table."""
+    batch, seq_q, hq, d = q.shape
+    ps, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    group = hq // hkv
+    out = [[[[0.0] * dv for _ in range(hq)] for _ in range(seq_q)] for _ in range(batch)]
+    lse = [[[-math.inf] * hq for _ in range(seq_q)] for _ in range(batch)]
+    for b in range(batch):
+        length = int(seq_lens[b])
+        for i in range(seq_q):
+            position = length - seq_q + i
+            for h in range(hq):
+                kvh = h // group
+                scores, rows = [], []
+                for j in range(length):
+                    if causal and j > position:
+                        continue
+                    page = int(block_table[b][j // ps])
+                    slot = j % ps
+                    dot = 0.0
+                    for e in range(d):
+                        dot += float(q[b, i, h, e]) * float(k_cache[page, slot, kvh, e])
+                    scores.append(dot * scale)
+                    rows.append([float(v_cache[page, slot, kvh, e]) for e in range(dv)])
+                if not scores:
+                    continue
+                top = max(scores)
+                weights = [math.exp(s - top) for s in scores]
+                total = sum(weights)
+                out[b][i][h] = [sum(w * r[e] for w, r in zip(weights, rows)) / total
+                                for e in range(dv)]
+                lse[b][i][h] = top + math.log(total)
+    return np.array(out), np.array(lse)
+
+
+# ----------------------------------------------------------------------------- checks
+def check_brute_force(seed=0):
+    rng = np.random.default_rng(seed)
+    cases = [
+        dict(batch=3, seq_q=1, hq=4, hkv=2, d=3, ps=2, causal=False),
+        dict(batch=2, seq_q=3, hq=2, hkv=1, d=4, ps=3, causal=True),
+        dict(batch=2, seq_q=2, hq=6, hkv=3, d=2, dv=3, ps=2, causal=True),
+        dict(batch=2, seq_q=1, hq=8, hkv=2, d=5, ps=4, causal=False),
+    ]
+    for c in cases:
+        causal = c.pop("causal")
+        p = random_problem(rng, **c)
+        args = (p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], p["scale"])
+        out, lse = O.attention(*args, causal)
+        bout, blse = brute_force(*args, causal)
+        _close(out, bout, 1e-12)
+        _close(lse, blse, 1e-12)
+
+
+def check_q_zero_decode(seed=1):
+    """q = 0: every valid score is 0, so lse = ln(L) and out = mean of the valid V rows."""
+    rng = np.random.default_rng(seed)
+    p = random_problem(rng, batch=5, hq=4, hkv=2, d=3, ps=3, lens=[1, 2, 7, 9, 12])
+    p["q"][:] = 0.0
+    out, lse = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                           p["scale"], False)
+    ps = p["k_cache"].shape[1]
+    for b, length in enumerate(p["seq_lens"]):
+        for h in range(4):
+            rows = [p["v_cache"][p["block_table"][b, j // ps], j % ps, h // 2] for j in range(length)]
+            _close(out[b, 0, h], np.mean(rows, axis=0), 1e-12)
+            _close(lse[b, 0, h], math.log(length), 1e-12)
+
+
+def check_q_zero_causal(seed=2):
+    """q = 0, causal bottom-right: row i sees min(L - Sq + i + 1, L) keys (none if <= 0)."""
+    rng = np.random.default_rng(seed)
+    for seq_q in (1, 3, 5):
+        p = random_problem(rng, batch=3, seq_q=seq_q, hq=2, hkv=2, d=2, ps=2, lens=[3, 5, 8])
+        p["q"][:] = 0.0
+        out, lse = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"],
+                               p["seq_lens"], p["scale"], True)
+        for b, length in enumerate(p["seq_lens"]):
+            for i in range(seq_q):
+                visible = min(length - seq_q + i + 1, length)
+                for h in range(2):
+                    if visible <= 0:
+                        assert lse[b, i, h] == -math.inf and (out[b, i, h] == 0).all()
+                        continue
+                    rows = [p["v_cache"][p["block_table"][b, j // 2], j % 2, h]
+                            for j in range(visible)]
+                    _close(out[b, i, h], np.mean(rows, axis=0), 1e-12)
+                    _close(lse[b, i, h], math.log(visible), 1e-12)
+
+
+def check_sdpa(seed=3):
+    """Unpaged special case against torch's float64 scaled_dot_product_attention."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(seed)
+    for seq_q, causal, group in ((1, False, 4), (6, True, 2), (1, False, 1)):
+        hkv = 2
+        length = 6 if causal else 11
+        p = random_problem(rng, batch=2, seq_q=seq_q, hq=hkv * group, hkv=hkv, d=8, ps=4,
+                           lens=[length, length])
+        out, _ = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                             p["scale"], causal)
+        kc = torch.from_numpy(p["k_cache"])
+        vc = torch.from_numpy(p["v_cache"])
+        tok = torch.arange(length)
+        for b in range(2):
+            pages = torch.from_numpy(p["block_table"][b])[tok // 4]
+            keys = kc[pages, tok % 4].repeat_interleave(group, dim=1)    # [L, Hq, D]
+            vals = vc[pages, tok % 4].repeat_interleave(group, dim=1)
+            qb = torch.from_numpy(p["q"][b]).transpose(0, 1)              # [Hq, Sq, D]
+            ref = F.scaled_dot_product_attention(qb, keys.transpose(0, 1), vals.transpose(0, 1),
+                                                 is_causal=causal, scale=p["scale"])
+            _close(out[b], ref.transpose(0, 1).numpy(), 1e-12)
+
+
+def check_shuffle_invariance(seed=4):
+    """Relabelling physical pages together with the table changes nothing, bit for bit."""
+    rng = np.random.default_rng(seed)
+    p = random_problem(rng, batch=4, seq_q=2, hq=4, hkv=2, d=3, ps=2, lens=[3, 0, 6, 9])
+    phys = p["k_cache"].shape[0]
+    relabel = rng.permutation(phys)               # old page id -> new page id
+    k2 = np.empty_like(p["k_cache"])
+    v2 = np.empty_like(p["v_cache"])
+    k2[relabel] = p["k_cache"]
+    v2[relabel] = p["v_cache"]
+    t2 = p["block_table"].copy()
+    mapped = t2 != UNMAPPED
+    t2[mapped] = relabel[t2[mapped]]
+    for causal in (False, True):
+        a = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                        p["scale"], causal)
+        b = O.attention(p["q"], k2, v2, t2, p["seq_lens"], p["scale"], causal)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def check_split_equivalence(seed=5):
+    """Combining the split partials reproduces the unsplit result for every S."""
+    rng = np.random.default_rng(seed)
+    for causal, seq_q in ((False, 1), (True, 4)):
+        p = random_problem(rng, batch=4, seq_q=seq_q, hq=4, hkv=2, d=3, ps=2,
+                           lens=[1, 4, 9, 16], width=8)
+        args = (p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], p["scale"],
+                causal)
+        out, lse = O.attention(*args)
+        for splits in range(1, 11):
+            po, pl = O.split_partials(*args, splits)
+            assert not np.isnan(po).any() and not np.isnan(pl).any()
+            co, cl = O.combine(po, pl)
+            _close(co, out, 1e-12)
+            _close(cl, lse, 1e-12)
+
+
+def check_v_ones(seed=6):
+    """V = 1 everywhere valid: every row with a valid key outputs exactly 1 (softmax rows sum to 1)."""
+    rng = np.random.default_rng(seed)
+    p = random_problem(rng, batch=3, seq_q=3, hq=4, hkv=2, d=3, ps=2, lens=[2, 5, 8], poison=False)
+    p["v_cache"][:] = 1.0
+    out, lse = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                           p["scale"], True)
+    valid = np.isfinite(lse)
+    assert valid.any()
+    _close(out[valid], np.ones_like(out[valid]), 1e-14)
+
+
+def check_empty():
+    """A sequence of length 0 yields output 0 and LSE -inf in every split."""
+    rng = np.random.default_rng(7)
+    p = random_problem(rng, batch=2, hq=2, hkv=1, d=2, ps=2, lens=[0, 3])
+    out, lse = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                           p["scale"], False)
+    assert (out[0] == 0).all() and (lse[0] == -math.inf).all()
+    assert np.isfinite(lse[1]).all()
+    po, pl = O.split_partials(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"],
+                              p["scale"], False, 3)
+    assert (po[0] == 0).all() and (pl[0] == -math.inf).all()
+
+
+def check_split_ranges():
+    """Ceiling division of pages per split with clamped ends."""
+    assert O.split_page_ranges(3, 2) == [(0, 2), (2, 3)]
+    assert O.split_page_ranges(5, 8) == [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 5), (5, 5),
+                                         (5, 5)]
+    assert O.split_page_ranges(0, 3) == [(0, 0), (0, 0), (0, 0)]
+    assert O.split_page_ranges(32, 4) == [(0, 8), (8, 16), (16, 24), (24, 32)]
+    # 17 tokens of 16-token pages, 8 splits: 2 pages, so splits 2..7 are empty
+    assert O.split_page_ranges(2, 8)[2:] == [(2, 2)] * 6
+    for n in range(0, 40):
+        for s in range(1, 12):
+            r = O.split_page_ranges(n, s)
+            assert r[0][0] == 0 and r[-1][1] == n
+            assert all(a <= b for a, b in r)
+            assert all(r[k][1] == r[k + 1][0] for k in range(s - 1))
+
+
+ALL_CHECKS = [
+    check_golden_hand,
+    check_golden_split,
+    check_golden_causal,
+    check_brute_force,
+    check_q_zero_decode,
+    check_q_zero_causal,
+    check_sdpa,
+    check_shuffle_invariance,
+    check_split_equivalence,
+    check_v_ones,
+    check_empty,
+    check_split_ranges,
+]

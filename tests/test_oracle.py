@@ -1,0 +1,10 @@
+"""The oracle against its pins (closed forms, brute force, torch SDPA, invariants)."""
+
+import pytest
+
+import oracle_pins
+
+
+@pytest.mark.parametrize("check", oracle_pins.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pin(check):
+    check()

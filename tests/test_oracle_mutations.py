@@ -1,0 +1,94 @@
+"""Plants plausible mistakes in the oracle (on the CPU) and requires the pins to catch each."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.paged_attention as O
+import oracle_pins
+
+_orig_attend = O.attend
+_orig_key_limit = O.key_limit
+_orig_gather = O.gather_logical
+
+
+def attend_no_scale(q_row, keys, values, scale):
+    return _orig_attend(q_row, keys, values, 1.0)
+
+
+def attend_sign_flip(q_row, keys, values, scale):
+    return _orig_attend(q_row, keys, values, -scale)
+
+
+def attend_lse_without_max(q_row, keys, values, scale):
+    o, lse = _orig_attend(q_row, keys, values, scale)
+    if keys.shape[0] == 0:
+        return o, lse
+    s = scale * (keys @ q_row)
+    return o, float(np.log(np.exp(s - s.max()).sum()))
+
+
+def attend_reversed_values(q_row, keys, values, scale):
+    return _orig_attend(q_row, keys, values[::-1], scale)
+
+
+def key_limit_off_by_one(seq_len, seq_q, row, causal):
+    if not causal:
+        return int(seq_len)
+    return max(0, min(int(seq_len), int(seq_len) - int(seq_q) + int(row)))
+
+
+def key_limit_top_left(seq_len, seq_q, row, causal):
+    if not causal:
+        return int(seq_len)
+    return max(0, min(int(seq_len), int(row) + 1))
+
+
+def gather_reversed_pages(cache, table_row, seq_len):
+    ps = cache.shape[1]
+    n = O.pages_for(seq_len, ps)
+    if n == 0:
+        return _orig_gather(cache, table_row, seq_len)
+    pages = [np.asarray(cache[int(table_row[s])], dtype=np.float64) for s in reversed(range(n))]
+    return np.concatenate(pages, axis=0)[: int(seq_len)]
+
+
+def split_floor_division(n_pages, num_splits):
+    per = int(n_pages) // int(num_splits)
+    return [(min(s * per, n_pages), min((s + 1) * per, n_pages)) for s in range(int(num_splits))]
+
+
+def combine_lse_double_max(part_out, part_lse):
+    out, lse = _orig_combine(part_out, part_lse)
+    m = np.max(np.asarray(part_lse), axis=-1)
+    return out, np.where(np.isfinite(lse), lse + np.where(np.isfinite(m), m, 0.0), lse)
+
+
+_orig_combine = O.combine
+
+MUTATIONS = [
+    ("kv_head_of", lambda q_head, group: q_head % group if group > 1 else q_head),
+    ("attend", attend_no_scale),
+    ("attend", attend_sign_flip),
+    ("attend", attend_lse_without_max),
+    ("attend", attend_reversed_values),
+    ("key_limit", key_limit_off_by_one),
+    ("key_limit", key_limit_top_left),
+    ("gather_logical", gather_reversed_pages),
+    ("split_page_ranges", split_floor_division),
+    ("combine", combine_lse_double_max),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTATIONS,
+                         ids=[f"{n}:{getattr(m, '__name__', 'lambda')}" for n, m in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(exc).__name__))
+    assert caught, f"no pin caught the planted mistake in {name}"

@@ -1,0 +1,60 @@
+"""Seeded generators: shapes, sentinels, poison and determinism (CPU)."""
+
+import math
+
+import torch
+
+from paged_kv_cache_195_amd.workloads import UNMAPPED_PAGE, make_workload
+
+
+def test_tiny_layout():
+    w = make_workload("tiny_f32")
+    assert w.q.shape == (2, 1, 4, 64) and w.k_cache.shape == (30, 16, 2, 64)
+    assert w.block_table.shape == (2, 16)
+    assert w.seq_lens_host == [37, 200]
+    t = w.table_host
+    assert (t[0, 3:] == UNMAPPED_PAGE).all() and (t[1, 13:] == UNMAPPED_PAGE).all()
+    used = torch.cat([t[0, :3], t[1, :13]])
+    assert len(set(used.tolist())) == 16 and int(used.max()) < 30
+    # unreferenced pages are NaN, referenced pages are finite up to each length
+    unused = sorted(set(range(30)) - set(used.tolist()))
+    assert torch.isnan(w.k_cache[unused]).all()
+    assert torch.isfinite(w.k_cache[t[1, :12].long()]).all()
+    last = int(t[0, 2])
+    assert torch.isfinite(w.k_cache[last, :5]).all() and torch.isnan(w.k_cache[last, 5:]).all()
+    assert math.isclose(w.scale, 1 / 8)
+
+
+def test_ragged_table_view_and_overstated_count():
+    w = make_workload("ragged_bf16")
+    assert w.block_table.shape == (8, 63) and w.block_table.stride() == (63, 1)
+    assert all(17 <= x <= 1000 for x in w.seq_lens_host)
+    storage = w.notes["table_storage"]
+    assert storage.numel() == 8 * 63 + 64 and (storage[8 * 63:] == UNMAPPED_PAGE).all()
+    assert w.num_pages_arg == 65538 > w.k_cache.shape[0]
+    assert w.k_cache.dtype == torch.bfloat16
+
+
+def test_prefill_layout():
+    w = make_workload("prefill_f16")
+    assert w.q.shape == (1, 1024, 1, 32) and w.k_cache.shape == (32, 32, 1, 32)
+    assert sorted(w.table_host[0].tolist()) == list(range(32))
+    assert w.table_host[0].tolist() != list(range(32))
+    assert w.causal
+
+
+def test_deterministic():
+    a = make_workload("tiny_f32")
+    b = make_workload("tiny_f32")
+    assert torch.equal(a.table_host, b.table_host)
+    assert torch.equal(torch.nan_to_num(a.k_cache), torch.nan_to_num(b.k_cache))
+    c = make_workload("tiny_f32", seed=11)
+    assert not torch.equal(torch.nan_to_num(a.q), torch.nan_to_num(c.q))
+
+
+def test_strided_table_variant():
+    w = make_workload("ragged_bf16", table_stride=70)
+    assert w.block_table.stride() == (70, 1)
+    storage = w.notes["table_storage"]
+    rows = storage[: 8 * 70].view(8, 70)
+    assert (rows[:, 63:] == UNMAPPED_PAGE).all()
