@@ -1,0 +1,210 @@
+"""Paged-decode benchmark on one MI355X.
+
+One step = one ``pa_decode`` call (split-KV attention over the paged cache,
+plus the LSE combine when the split count is above 1) over one batch of the
+Llama-3-8B decode shape: B=256, Hq=32, Hkv=8, D=128, bf16, 16-token pages,
+4096 keys per sequence, K and V caches of exactly 2 GiB each addressed
+through a seeded random permutation of all 65,536 pages.  Inputs are
+resident in HBM before the timed region starts.
+
+Prints one JSON line: KV-read GB/s (algorithmic K+V bytes per step divided by
+the step time), microseconds per step, the roofline entry of the attention
+kernel, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_traffic.md")
+KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    fields = dict(re.findall(r"^\s*[-*]?\s*`?(\w+)`?\s*[:=]\s*`?([0-9a-f.e+]+)`?\s*$", text, re.M))
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
+    """Time the oracle on whole sequences of the same workload until about
+    ``budget_s`` of wall time is spent; also report its agreement with the GPU."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle.paged_attention as O
+
+    ps = w.k_cache.shape[1]
+    batch = w.q.shape[0]
+    # spread the sample over the batch first, then fill in
+    order = []
+    for b in list(range(0, batch, max(1, batch // 64))) + list(range(batch)):
+        if b not in order:
+            order.append(b)
+
+    def host_pages(cache, rows):
+        ids = sorted({int(x) for b in rows for x in w.table_host[b, : -(-w.seq_lens_host[b] // ps)]})
+        pages = cache.index_select(0, torch.tensor(ids, device=cache.device)).float().cpu().numpy()
+        lut = {pid: pages[i] for i, pid in enumerate(ids)}
+
+        class Pages:
+            shape = tuple(cache.shape)
+
+            def __getitem__(self, pid):
+                return lut[int(pid)]
+        return Pages()
+
+    def one(b, kp, vp):
+        return O.attention(w.q[b:b + 1].float().cpu().numpy(), kp, vp,
+                           w.table_host[b:b + 1].numpy(), np.array(w.seq_lens_host[b:b + 1]),
+                           w.scale, w.causal)
+
+    done, elapsed, max_err, tokens = [], 0.0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s and len(done) < batch:
+            rows = order[len(done): len(done) + threads]
+            kp, vp = host_pages(w.k_cache, rows), host_pages(w.v_cache, rows)
+            t0 = time.perf_counter()
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                res = list(ex.map(lambda b: one(b, kp, vp), rows))
+            elapsed += time.perf_counter() - t0
+            for b, (xo, _) in zip(rows, res):
+                y = out_gpu[b].float().cpu().numpy()
+                max_err = max(max_err, float(np.abs(y - xo[0, 0]).max()))
+                tokens += w.seq_lens_host[b]
+            done.extend(rows)
+    per_token = 2 * w.k_cache.shape[2] * w.k_cache.shape[3] * w.k_cache.element_size()
+    return {
+        "value": round(tokens * per_token / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(done)} of {batch} sequences (whole sequences, all heads), f64 NumPy, "
+                  f"{threads} threads x 1 BLAS thread, {elapsed:.1f} s wall",
+        "max_abs_err_vs_gpu": max_err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--splits", type=int, default=0, help="split-KV count (0 = automatic)")
+    ap.add_argument("--variant", default=None, help="'contiguous' for an identity page order")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the paged decode path "
+              "is single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_195_amd as pa
+    from paged_kv_cache_195_amd.workloads import kv_bytes, make_workload
+
+    torch.cuda.set_device(0)
+    w = make_workload("llama3_8b_decode", device="cuda", variant=args.variant)
+    shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
+    splits = pa.resolve_num_splits(shape, args.splits)
+    ws_bytes = pa.workspace_bytes(shape, args.splits)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.q.shape[0], 1, w.q.shape[2], w.v_cache.shape[3]), dtype=w.q.dtype,
+                      device="cuda")
+    lse = torch.empty(out.shape[:3], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
+                  num_splits=args.splits, out=out, lse=lse, workspace=workspace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    nbytes = kv_bytes(w)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v, seeded random page permutation",
+        "config": {
+            "workload": "llama3_8b_decode: B=256 Hq=32 Hkv=8 D=128 bf16 page16 Skv=4096, "
+                        "K and V caches 2 GiB each (65,536 pages)",
+            "batch": w.q.shape[0], "seq_kv": 4096, "num_q_heads": 32, "num_kv_heads": 8,
+            "head_dim": 128, "page_size": 16, "num_splits": splits,
+            "page_order": args.variant or "random",
+            "kv_bytes_per_step": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic() if splits == 1 else None,
+        },
+    }
+    if splits > 1:
+        line["roofline"]["note"] = "step = attention + combine kernels"
+    if not args.no_cpu_baseline:
+        threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+        line["cpu_baseline"] = cpu_baseline(w, out[:, 0], args.cpu_budget, threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

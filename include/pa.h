@@ -1,0 +1,179 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention library (libpa.so).
+ *
+ * The library computes softmax(scale * Q K^T) V over a K/V cache that is
+ * scattered in fixed-size pages and addressed through a per-sequence block
+ * table, with grouped-query heads, ragged lengths, causal masking and
+ * split-KV partials merged by a log-sum-exp combine.
+ *
+ * Sources of the operation (page title, section):
+ *  - paged K/V as a lazy view over page addresses, dereferenced at tile
+ *    lowering: rocMLIR "Paged Attention: migraphx & highlevel pipeline
+ *    changes", Technical Details (rock.deref, rock.attention keyAddresses /
+ *    valueAddresses);
+ *  - the result is attention over the logical-order cache: rocMLIR "Paged
+ *    Attention: rocmlir-gen changes", Technical Details, CPU Validation;
+ *  - pages holding every kv head, ragged lengths, an unmapped id in the
+ *    table's tail, caches past 2 GiB: rocm-libraries "one K/V resource per
+ *    page on the gfx942 2D i64 path", Motivation and Coverage;
+ *  - split ranges by ceiling division, empty splits, the -inf - (-inf) and
+ *    0/0 guards, the f32 combine: rocMLIR "Fix split-kv attention masking and
+ *    sweep RMS", Technical Details.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *    allocates nothing and keeps no state between calls; it is thread-safe.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without waiting for it.
+ *  - Every argument check runs on the host before anything is launched.  A
+ *    failed check returns a negative pa_status and writes nothing.  A launch
+ *    failure returns PA_EHIP.  No C++ exception crosses this interface.
+ *  - q, k_cache and v_cache must be 16-byte aligned (else PA_EINVAL).
+ *  - Tensors are dense and row-major unless a stride is given:
+ *      q            [B, Sq, Hq, D]                 dtype
+ *      k_cache      [num_pages, page_size, Hkv, D]  dtype
+ *      v_cache      [num_pages, page_size, Hkv, Dv] dtype
+ *      block_table  [B, W] int32, row stride block_table_stride (>= W)
+ *      seq_lens     [B] int32
+ *      out          [B, Sq, Hq, Dv]                dtype
+ *      lse          [B, Sq, Hq] float32 natural-log LSE (may be NULL)
+ *    Query head h reads kv head h / (Hq / Hkv).
+ *  - Device-side preconditions (the caller's contract, not checked):
+ *      0 <= seq_lens[b] <= W * page_size, and
+ *      0 <= block_table[b][s] < num_pages for s < ceil(seq_lens[b] / page_size).
+ *    Slots at or past ceil(seq_lens[b] / page_size) are never read and may
+ *    hold anything (e.g. an unmapped id such as 0x7FFFFFFF).  Token slots of a
+ *    last page past seq_lens[b] are never used, even if they hold NaN.
+ *  - A row with no valid key (seq_lens[b] == 0, or a causal row placed before
+ *    the first key) gets out = 0 and lse = -inf.
+ *  - Page bases are formed as zero-extended page id times page bytes in
+ *    64-bit arithmetic, so caches larger than 2 GiB (and 4 GiB) are read
+ *    correctly.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k_cache, v_cache and out. */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Return codes. */
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = -1,       /* a null pointer, a non-positive size, Hq % Hkv != 0,
+                           stride < W, a size overflow, a non-finite scale,
+                           num_splits out of range, seq_q != 1 in pa_decode   */
+  PA_EUNSUPPORTED = -2, /* valid but outside the compiled envelope            */
+  PA_EWORKSPACE = -3,   /* workspace NULL or smaller than pa_workspace_bytes  */
+  PA_EHIP = -4          /* the HIP runtime refused a launch                   */
+} pa_status;
+
+/* Problem shape shared by pa_decode, pa_prefill and pa_workspace_bytes. */
+typedef struct pa_shape {
+  int32_t dtype;              /* a pa_dtype                                     */
+  int32_t batch;              /* B                                              */
+  int32_t seq_q;              /* Sq: query rows per sequence (1 for decode)     */
+  int32_t num_q_heads;        /* Hq                                             */
+  int32_t num_kv_heads;       /* Hkv, divides Hq                                */
+  int32_t head_dim_qk;        /* D                                              */
+  int32_t head_dim_v;         /* Dv                                             */
+  int32_t page_size;          /* tokens per page                                */
+  int64_t num_pages;          /* physical pages per cache tensor (validation)   */
+  int32_t max_pages_per_seq;  /* W: block-table width                           */
+  int64_t block_table_stride; /* elements between block-table rows, >= W        */
+} pa_shape;
+
+/*
+ * Supported envelope of this build (else PA_EUNSUPPORTED):
+ *   dtype F32, F16 or BF16; D == Dv in {32, 64, 128}; page_size in {16, 32};
+ *   any group size Hq / Hkv >= 1; B <= 65535 and Hkv <= 65535.
+ */
+
+/*
+ * pa_decode -- one new query token per sequence (Sq == 1) over its paged
+ * cache: grouped-query decode with ragged lengths.  The split-KV form of the
+ * decode step follows rocMLIR "Fix split-kv attention masking and sweep RMS"
+ * (Technical Details) and the page-table loading follows rocm-libraries "one
+ * K/V resource per page on the gfx942 2D i64 path" (Technical Details,
+ * Changes): each page id is read once and turned into a 64-bit page base.
+ *
+ *  shape       problem shape; shape->seq_q must be 1.
+ *  q, k_cache, v_cache, block_table, seq_lens, out: as in the table above.
+ *  scale       multiplies q . k before the softmax; must be finite.
+ *  causal      accepted for a uniform signature; with one query row per
+ *              sequence, bottom-right causal masking keeps every key.
+ *  num_splits  0 = pick automatically (see pa_resolve_num_splits); else the
+ *              number S >= 1 of split-KV partitions of each sequence's pages.
+ *              Split s covers pages [s*P, min((s+1)*P, n)) with
+ *              n = ceil(seq_lens[b] / page_size) and P = ceil(n / S); splits
+ *              past n are empty and contribute nothing.
+ *  lse         optional [B, 1, Hq] float32 output.
+ *  workspace   device scratch of at least pa_workspace_bytes(shape, S) bytes
+ *              (NULL allowed when that is 0).  When S > 1 the partials are
+ *              left in it: part_out [B*Sq*Hq, S, Dv] float32 at offset 0, then
+ *              part_lse [B*Sq*Hq, S] float32 at the next 256-byte boundary
+ *              (per split: output normalised by its own softmax sum, LSE in
+ *              natural log; an empty split holds 0 and -inf).
+ *  stream      hipStream_t or NULL.
+ */
+int pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
+              int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * pa_prefill -- Sq >= 1 query rows per sequence, the last Sq positions of a
+ * sequence of seq_lens[b] keys.  With causal != 0 the mask is bottom-right
+ * aligned: row i sits at key position seq_lens[b] - Sq + i and sees keys up
+ * to and including it.  Per-row validity follows rocMLIR "Fix split-kv
+ * attention masking and sweep RMS" (Technical Details, host reference:
+ * causal valid-split masking); the paged prefill shape follows rocMLIR
+ * "Paged Attention: rocmlir-gen changes" (Example Usage).  Arguments and
+ * workspace as for pa_decode; lse is [B, Sq, Hq].
+ */
+int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
+               int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * pa_combine -- log-sum-exp merge of split-KV partials, in float32 for every
+ * storage type, cast to `dtype` once at the end (rocMLIR "Fix split-kv
+ * attention masking and sweep RMS", Technical Details, host reference: f32
+ * combine for narrow floats).  Per row: M = max_s lse_s; if M == -inf the
+ * row is empty and gets out = 0, lse = -inf; else w_s = exp(lse_s - M),
+ * out = sum_s w_s * o_s / sum_s w_s, lse = M + ln(sum_s w_s).
+ *
+ *  dtype       pa_dtype of out.
+ *  rows        number of rows (> 0); num_splits S (> 0); head_dim_v Dv (> 0).
+ *  part_out    [rows, S, Dv] float32.   part_lse [rows, S] float32.
+ *  out         [rows, Dv] dtype.        lse      [rows] float32 or NULL.
+ */
+int pa_combine(int32_t dtype, int32_t rows, int32_t num_splits, int32_t head_dim_v,
+               const float* part_out, const float* part_lse, void* out, float* lse,
+               void* stream);
+
+/* Workspace bytes pa_decode / pa_prefill need for `num_splits` (0 = auto);
+ * 0 when the resolved split count is 1 or the shape is invalid. */
+size_t pa_workspace_bytes(const pa_shape* shape, int num_splits);
+
+/* The split count a call with `num_splits` uses: `num_splits` itself when it
+ * is > 0, else the automatic choice, which depends on the shape only (never
+ * on device data), so it is known on the host without a synchronisation.
+ * Negative pa_status for an invalid shape or num_splits. */
+int pa_resolve_num_splits(const pa_shape* shape, int num_splits);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

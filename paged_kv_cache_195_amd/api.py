@@ -1,0 +1,216 @@
+"""ctypes binding of libpa.so (the C ABI in include/pa.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+a ``pa_shape``; output, LSE and workspace tensors are allocated with torch
+when the caller does not pass them; the current torch stream is handed to the
+library.  Every step of the computation runs in the HIP kernels.  There is no
+fallback: if the library is missing, or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, -1, -2, -3, -4
+DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+# The functions include/pa.h declares.
+EXPORTS = ("pa_decode", "pa_prefill", "pa_combine", "pa_workspace_bytes",
+           "pa_resolve_num_splits", "pa_strerror")
+
+
+class PaShape(ctypes.Structure):
+    """Mirror of ``pa_shape``."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seq_q", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("block_table_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m paged_kv_cache_195_amd.build` first")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    shape_p = ctypes.POINTER(PaShape)
+    attn_args = [shape_p, vp, vp, vp, vp, vp, f32, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.pa_decode.argtypes = attn_args
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = attn_args
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.pa_combine.restype = ctypes.c_int
+    lib.pa_workspace_bytes.argtypes = [shape_p, ctypes.c_int]
+    lib.pa_workspace_bytes.restype = sz
+    lib.pa_resolve_num_splits.argtypes = [shape_p, ctypes.c_int]
+    lib.pa_resolve_num_splits.restype = ctypes.c_int
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.pa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().pa_strerror(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != PA_OK:
+        raise RuntimeError(f"{what} failed: {strerror(status)} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_shape(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_table: torch.Tensor, num_pages: Optional[int] = None) -> PaShape:
+    """``pa_shape`` of a call; ``q`` is ``[B, Sq, Hq, D]``."""
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Sq,Hq,D], caches [P,page,Hkv,D], block_table [B,W]")
+    if q.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    s = PaShape()
+    s.dtype = DTYPE_CODE[q.dtype]
+    s.batch, s.seq_q, s.num_q_heads, s.head_dim_qk = q.shape
+    s.num_kv_heads = k_cache.shape[2]
+    s.head_dim_v = v_cache.shape[3]
+    s.page_size = k_cache.shape[1]
+    s.num_pages = k_cache.shape[0] if num_pages is None else int(num_pages)
+    s.max_pages_per_seq = block_table.shape[1]
+    s.block_table_stride = block_table.stride(0)
+    return s
+
+
+def _validate_tensors(q, k_cache, v_cache, block_table, seq_lens):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if block_table.dtype != torch.int32 or not block_table.is_cuda or block_table.stride(1) != 1:
+        raise ValueError("block_table must be an int32 GPU tensor with unit column stride")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 GPU tensor")
+    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+
+
+def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causal, num_splits,
+               out, lse, num_pages, workspace, return_workspace):
+    lib = load_library()
+    _validate_tensors(q, k_cache, v_cache, block_table, seq_lens)
+    shape = make_shape(q, k_cache, v_cache, block_table, num_pages)
+    batch, seq_q, hq, _ = q.shape
+    dv = v_cache.shape[3]
+    if out is None:
+        out = torch.empty((batch, seq_q, hq, dv), dtype=q.dtype, device=q.device)
+    elif not out.is_contiguous() or out.dtype != q.dtype or out.numel() != batch * seq_q * hq * dv:
+        raise ValueError("out must be a contiguous [B, Sq, Hq, Dv] tensor of q's dtype")
+    if lse is None:
+        lse = torch.empty((batch, seq_q, hq), dtype=torch.float32, device=q.device)
+    elif not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != batch * seq_q * hq:
+        raise ValueError("lse must be a contiguous float32 [B, Sq, Hq] tensor")
+    need = int(lib.pa_workspace_bytes(ctypes.byref(shape), int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = getattr(lib, fn_name)(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), ctypes.c_float(scale), int(bool(causal)), int(num_splits), _ptr(out),
+        _ptr(lse), _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+    _check(status, fn_name)
+    if return_workspace:
+        return out, lse, workspace
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = False,
+           num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
+           workspace=None, return_workspace: bool = False):
+    """Paged decode.  ``q`` is ``[B, Hq, D]`` or ``[B, 1, Hq, D]``; returns
+    ``(out, lse)`` shaped like ``q`` (``lse`` without the head-dim axis)."""
+    squeeze = q.dim() == 3
+    q4 = q.unsqueeze(1) if squeeze else q
+    res = _attention("pa_decode", q4, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                     num_splits, out, lse, num_pages, workspace, return_workspace)
+    if squeeze:
+        res = (res[0].squeeze(1), res[1].squeeze(1)) + tuple(res[2:])
+    return res
+
+
+def prefill(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = True,
+            num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
+            workspace=None, return_workspace: bool = False):
+    """Paged prefill: ``q [B, Sq, Hq, D]`` are the last Sq positions of each sequence."""
+    return _attention("pa_prefill", q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                      num_splits, out, lse, num_pages, workspace, return_workspace)
+
+
+def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,
+            out=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """LSE merge of ``part_out [rows, S, Dv]`` / ``part_lse [rows, S]`` (float32)."""
+    lib = load_library()
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not (part_out.is_contiguous() and part_lse.is_contiguous() and part_out.is_cuda):
+        raise ValueError("partials must be contiguous GPU tensors")
+    rows, splits, dv = part_out.shape
+    if tuple(part_lse.shape) != (rows, splits):
+        raise ValueError("part_lse must be [rows, S]")
+    if out is None:
+        out = torch.empty((rows, dv), dtype=dtype, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=part_out.device)
+    stream = torch.cuda.current_stream(part_out.device).cuda_stream
+    status = lib.pa_combine(DTYPE_CODE[dtype], rows, splits, dv, _ptr(part_out), _ptr(part_lse),
+                            _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    _check(status, "pa_combine")
+    return out, lse
+
+
+def workspace_bytes(shape: PaShape, num_splits: int = 0) -> int:
+    return int(load_library().pa_workspace_bytes(ctypes.byref(shape), int(num_splits)))
+
+
+def resolve_num_splits(shape: PaShape, num_splits: int = 0) -> int:
+    return int(load_library().pa_resolve_num_splits(ctypes.byref(shape), int(num_splits)))
+
+
+def split_views(workspace: torch.Tensor, rows: int, num_splits: int, head_dim_v: int):
+    """``(part_out, part_lse)`` float32 views of a workspace left by a split call
+    (layout documented in include/pa.h)."""
+    n_out = rows * num_splits * head_dim_v
+    lse_off = (n_out * 4 + 255) // 256 * 256
+    flat = workspace.view(torch.uint8)
+    part_out = flat[: n_out * 4].view(torch.float32).view(rows, num_splits, head_dim_v)
+    part_lse = flat[lse_off: lse_off + rows * num_splits * 4].view(torch.float32)
+    return part_out, part_lse.view(rows, num_splits)

@@ -1,0 +1,11 @@
+// Vector-ALU paged attention kernels for f16_t elements.
+#include "attn_valu_launch.h"
+
+namespace pa {
+
+hipError_t launch_attn_valu_f16(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                               int page_size, int batch, hipStream_t stream) {
+  return launch_attn_valu_t<f16_t>(p, plan, head_dim, page_size, batch, stream);
+}
+
+}  // namespace pa

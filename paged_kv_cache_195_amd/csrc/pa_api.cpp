@@ -1,0 +1,225 @@
+// Host side of the C ABI declared in include/pa.h: argument validation,
+// split planning, workspace layout and kernel dispatch.  Nothing here touches
+// the GPU until every check has passed; nothing is allocated.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+// Workgroups that keep every compute unit of an MI355X (256 CUs) busy with a
+// few resident workgroups each; the automatic split count aims at this.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int kMaxSplits = 256;
+constexpr int kMaxAutoSplits = 64;
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Rows per workgroup: the smallest power of two >= the rows that share a kv
+// head, at most 8.
+int rows_per_wg(int64_t rows_per_kvh) {
+  int mr = 1;
+  while (mr < rows_per_kvh && mr < 8) mr *= 2;
+  return mr;
+}
+
+// Shape checks common to decode and prefill.  Returns PA_OK or an error.
+int check_shape(const pa_shape* s, bool decode) {
+  if (s == nullptr) return PA_EINVAL;
+  if (s->dtype != PA_F32 && s->dtype != PA_F16 && s->dtype != PA_BF16) return PA_EINVAL;
+  if (s->batch <= 0 || s->seq_q <= 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 ||
+      s->head_dim_qk <= 0 || s->head_dim_v <= 0 || s->page_size <= 0 || s->num_pages <= 0 ||
+      s->max_pages_per_seq <= 0)
+    return PA_EINVAL;
+  if (decode && s->seq_q != 1) return PA_EINVAL;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_EINVAL;
+  if (s->block_table_stride < s->max_pages_per_seq) return PA_EINVAL;
+  // W * page_size tokens must fit in int32 (sequence positions are int32).
+  if (static_cast<int64_t>(s->max_pages_per_seq) * s->page_size > INT32_MAX) return PA_EINVAL;
+  // Flat row indices B * Sq * Hq and element offsets inside q/out fit int32 / int64.
+  const int64_t rows = static_cast<int64_t>(s->batch) * s->seq_q * s->num_q_heads;
+  if (rows > INT32_MAX) return PA_EINVAL;
+  // The byte size of one cache tensor must be representable.
+  const int64_t elem = s->dtype == PA_F32 ? 4 : 2;
+  const int64_t page_bytes =
+      static_cast<int64_t>(s->page_size) * s->num_kv_heads * s->head_dim_qk * elem;
+  if (page_bytes > INT32_MAX) return PA_EINVAL;
+  if (s->num_pages > INT64_MAX / page_bytes) return PA_EINVAL;
+  if (static_cast<int64_t>(s->batch - 1) * s->block_table_stride >
+      INT64_MAX - s->max_pages_per_seq)
+    return PA_EINVAL;
+  // Envelope of the compiled kernels (grid y = Hkv and z = B are 16-bit).
+  if (s->batch > 65535 || s->num_kv_heads > 65535) return PA_EUNSUPPORTED;
+  if (s->head_dim_qk != s->head_dim_v) return PA_EUNSUPPORTED;
+  if (!pa::attn_valu_supported(s->head_dim_qk, s->page_size)) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
+  pa::AttnPlan plan;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
+  plan.rows_per_wg = rows_per_wg(rows_per_kvh);
+  plan.row_groups = static_cast<int>((rows_per_kvh + plan.rows_per_wg - 1) / plan.rows_per_wg);
+  if (num_splits > 0) {
+    plan.num_splits = num_splits;
+  } else {
+    const int64_t units = static_cast<int64_t>(s->batch) * s->num_kv_heads * plan.row_groups;
+    int64_t want = (kTargetWorkgroups + units - 1) / units;
+    if (want > s->max_pages_per_seq) want = s->max_pages_per_seq;
+    if (want > kMaxAutoSplits) want = kMaxAutoSplits;
+    plan.num_splits = want < 1 ? 1 : static_cast<int>(want);
+  }
+  return plan;
+}
+
+size_t workspace_for(const pa_shape* s, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(s->batch) * s->seq_q * s->num_q_heads;
+  const size_t part = rows * static_cast<size_t>(splits) * s->head_dim_v * sizeof(float);
+  return align_up(part) + rows * static_cast<size_t>(splits) * sizeof(float);
+}
+
+int check_splits(int num_splits) {
+  return (num_splits < 0 || num_splits > kMaxSplits) ? PA_EINVAL : PA_OK;
+}
+
+int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  float scale, int causal, int num_splits, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(s, decode);
+  if (st != PA_OK) return st;
+  st = check_splits(num_splits);
+  if (st != PA_OK) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || out == nullptr)
+    return PA_EINVAL;
+  if (!isfinite(scale)) return PA_EINVAL;
+  // q, k_cache and v_cache are read in 16-byte chunks.
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
+
+  const pa::AttnPlan plan = plan_for(s, num_splits);
+  const size_t need = workspace_for(s, plan.num_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_EWORKSPACE;
+
+  const int group = s->num_q_heads / s->num_kv_heads;
+  pa::AttnParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.lse = lse;
+  p.part_out = nullptr;
+  p.part_lse = nullptr;
+  if (plan.num_splits > 1) {
+    const size_t rows = static_cast<size_t>(s->batch) * s->seq_q * s->num_q_heads;
+    p.part_out = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(
+        static_cast<char*>(workspace) +
+        align_up(rows * static_cast<size_t>(plan.num_splits) * s->head_dim_v * sizeof(float)));
+  }
+  p.bt_stride = s->block_table_stride;
+  p.seq_q = s->seq_q;
+  p.num_q_heads = s->num_q_heads;
+  p.num_kv_heads = s->num_kv_heads;
+  p.group = group;
+  p.rows_per_kvh = s->seq_q * group;
+  p.num_splits = plan.num_splits;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (s->dtype) {
+    case PA_F32:
+      err = pa::launch_attn_valu_f32(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+      break;
+    case PA_F16:
+      err = pa::launch_attn_valu_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+      break;
+    default:
+      err = pa::launch_attn_valu_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+      break;
+  }
+  if (err != hipSuccess) return PA_EHIP;
+  if (plan.num_splits > 1) {
+    const int rows = s->batch * s->seq_q * s->num_q_heads;
+    err = pa::launch_combine(s->dtype, rows, plan.num_splits, s->head_dim_v, p.part_out,
+                             p.part_lse, out, lse, hs);
+    if (err != hipSuccess) return PA_EHIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+bool pa::attn_valu_supported(int head_dim, int page_size) {
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
+         (page_size == 16 || page_size == 32);
+}
+
+extern "C" {
+
+int pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
+              int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return run_attention(shape, true, q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                       num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
+               int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  return run_attention(shape, false, q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                       num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int pa_combine(int32_t dtype, int32_t rows, int32_t num_splits, int32_t head_dim_v,
+               const float* part_out, const float* part_lse, void* out, float* lse,
+               void* stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_EINVAL;
+  if (rows <= 0 || num_splits <= 0 || head_dim_v <= 0) return PA_EINVAL;
+  if (part_out == nullptr || part_lse == nullptr || out == nullptr) return PA_EINVAL;
+  const hipError_t err = pa::launch_combine(dtype, rows, num_splits, head_dim_v, part_out,
+                                            part_lse, out, lse, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+size_t pa_workspace_bytes(const pa_shape* shape, int num_splits) {
+  if (check_shape(shape, false) != PA_OK || check_splits(num_splits) != PA_OK) return 0;
+  return workspace_for(shape, plan_for(shape, num_splits).num_splits);
+}
+
+int pa_resolve_num_splits(const pa_shape* shape, int num_splits) {
+  int st = check_shape(shape, false);
+  if (st != PA_OK) return st;
+  st = check_splits(num_splits);
+  if (st != PA_OK) return st;
+  return plan_for(shape, num_splits).num_splits;
+}
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "shape or dtype outside the compiled envelope";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+// Host and device code both include this file; it holds no device code.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one attention launch needs.  Pointers are device memory.
+struct AttnParams {
+  const void* q;               // [B, Sq, Hq, D]
+  const void* k;               // [num_pages, page_size, Hkv, D]
+  const void* v;               // [num_pages, page_size, Hkv, Dv]
+  const int32_t* block_table;  // row b at block_table + b * bt_stride
+  const int32_t* seq_lens;     // [B]
+  void* out;                   // [B, Sq, Hq, Dv]           (num_splits == 1)
+  float* lse;                  // [B, Sq, Hq] or nullptr     (num_splits == 1)
+  float* part_out;             // [B*Sq*Hq, S, Dv]           (num_splits > 1)
+  float* part_lse;             // [B*Sq*Hq, S]               (num_splits > 1)
+  int64_t bt_stride;
+  int32_t seq_q;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // Hq / Hkv
+  int32_t rows_per_kvh;        // Sq * group: query rows that share one kv head
+  int32_t num_splits;          // S >= 1
+  int32_t causal;
+  float scale_log2;            // scale * log2(e): scores are kept in base 2
+};
+
+// Launch shape chosen on the host.
+struct AttnPlan {
+  int rows_per_wg;   // MR: query rows (position, head) one workgroup carries
+  int row_groups;    // ceil(rows_per_kvh / MR)
+  int num_splits;    // S
+};
+
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Grid = (S * row_groups, Hkv, B); returns a hipError_t.
+hipError_t launch_attn_valu_f32(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                int page_size, int batch, hipStream_t stream);
+hipError_t launch_attn_valu_f16(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                int page_size, int batch, hipStream_t stream);
+hipError_t launch_attn_valu_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                 int page_size, int batch, hipStream_t stream);
+
+// True when the (head_dim, page_size) pair has a compiled kernel.
+bool attn_valu_supported(int head_dim, int page_size);
+
+hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
+                          const float* part_out, const float* part_lse, void* out, float* lse,
+                          hipStream_t stream);
+
+}  // namespace pa

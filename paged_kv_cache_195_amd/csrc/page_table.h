@@ -1,0 +1,39 @@
+// Page-table loader: one block-table read per page, one 64-bit page base.
+//
+// A sequence's keys live in pages of `page_size` tokens; slot s of its
+// block-table row names the physical page that holds tokens
+// [s * page_size, (s + 1) * page_size).  The loader follows the per-page
+// design of rocm-libraries "one K/V resource per page on the gfx942 2D i64
+// path" (Technical Details, Changes): the page id is read once for the whole
+// page and every copy from that page is (page base, offset inside the page).
+// Differences from that design, for gfx950:
+//  * the id is read by the wave with a uniform (scalar) load and is never
+//    re-read per copy, so no wait on it drains the in-flight K/V loads;
+//  * the base is the zero-extended id times the page's byte size, formed in
+//    64-bit arithmetic, so a cache of any size up to 2^63 bytes is addressed
+//    correctly (the page above shows sign extension failing past 2^31 bytes);
+//  * only slots below the sequence's own page count are ever read, a stricter
+//    bound than one over the whole table, so an unmapped id in a slot past the
+//    sequence (or in the table's tail) is never dereferenced.
+// In-page offsets stay 32-bit: a page is far below 4 GiB.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct PageTable {
+  const int32_t* row;   // this sequence's block-table row
+  int64_t page_bytes;   // bytes of one page of one cache tensor
+  int n_pages;          // ceil(seq_len / page_size): slots that may be read
+
+  // Byte offset of the page in slot `slot` from the start of the cache.
+  // The caller guarantees 0 <= slot < n_pages; `slot` is wave-uniform.
+  __device__ __forceinline__ int64_t base(int slot) const {
+    const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(row[slot]));
+    return static_cast<int64_t>(static_cast<uint64_t>(id)) * page_bytes;
+  }
+};
+
+}  // namespace pa

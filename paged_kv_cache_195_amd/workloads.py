@@ -227,3 +227,46 @@ def kv_bytes(inputs: PagedInputs) -> int:
     spec = inputs.spec
     per_token = spec.num_kv_heads * spec.head_dim * inputs.k_cache.element_size()
     return 2 * per_token * sum(inputs.seq_lens_host)
+
+
+def make_custom(dtype: str, seq_lens: List[int], num_q_heads: int, num_kv_heads: int,
+                head_dim: int, page_size: int, seq_q: int = 1, causal: bool = False,
+                width: Optional[int] = None, extra_pages: int = 5, seed: int = 0,
+                device="cpu", table_stride: Optional[int] = None) -> PagedInputs:
+    """Any shape, same recipe as the named workloads (shuffled pages, unmapped
+    unused slots, NaN in unreferenced pages and in last-page tails)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdtype = DTYPES[dtype]
+    ps = page_size
+    n_per = [-(-x // ps) for x in seq_lens]
+    width = max(max(n_per, default=0), 1) if width is None else width
+    if max(n_per, default=0) > width:
+        raise ValueError("sequence longer than the block table allows")
+    bsz = len(seq_lens)
+    total_used = sum(n_per)
+    phys = total_used + extra_pages
+    perm = torch.randperm(phys, generator=gen, device=device)
+    stride = width if table_stride is None else int(table_stride)
+    storage = torch.full((bsz * stride + 64,), UNMAPPED_PAGE, dtype=torch.int32, device=device)
+    used = perm[:total_used].to(torch.int32)
+    rows = storage[: bsz * stride].view(bsz, stride)
+    pos = 0
+    for b, n in enumerate(n_per):
+        rows[b, :n] = used[pos:pos + n]
+        pos += n
+    table = rows[:, :width]
+    q = _normal(gen, (bsz, seq_q, num_q_heads, head_dim), tdtype, device)
+    k_cache = _normal(gen, (phys, ps, num_kv_heads, head_dim), tdtype, device)
+    v_cache = _normal(gen, (phys, ps, num_kv_heads, head_dim), tdtype, device)
+    _poison_unused(k_cache, used, list(seq_lens), table, ps)
+    _poison_unused(v_cache, used, list(seq_lens), table, ps)
+    spec = WorkloadSpec("custom", dtype, bsz, seq_q, num_q_heads, num_kv_heads, head_dim, ps,
+                        causal, (1,), seed, "custom")
+    inputs = PagedInputs(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache, block_table=table,
+                         seq_lens=torch.tensor(list(seq_lens), dtype=torch.int32, device=device),
+                         scale=1.0 / math.sqrt(head_dim), causal=causal, num_pages_arg=phys,
+                         seq_lens_host=list(seq_lens), table_host=table.cpu())
+    inputs.notes["true_num_pages"] = phys
+    inputs.notes["table_storage"] = storage
+    return inputs
