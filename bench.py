@@ -117,6 +117,27 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
     }
 
 
+def copy_calibration(mib: int, steps: int):
+    """A plain copy of a known size: HBM counters read on it give the factor
+    between counter units and bytes."""
+    import torch
+
+    n = mib * 2 ** 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": steps,
+                      "ms_per_copy": round(ms, 5), "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +147,8 @@ def main():
     ap.add_argument("--variant", default=None, help="'contiguous' for an identity page order")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,6 +162,9 @@ def main():
     from paged_kv_cache_195_amd.workloads import kv_bytes, make_workload
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     w = make_workload("llama3_8b_decode", device="cuda", variant=args.variant)
     shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
     splits = pa.resolve_num_splits(shape, args.splits)
