@@ -144,7 +144,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--splits", type=int, default=0, help="split-KV count (0 = automatic)")
-    ap.add_argument("--variant", default=None, help="'contiguous' for an identity page order")
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    choices=["llama3_8b_decode", "qwen3_235b_decode", "ragged_bf16", "tiny_f32"],
+                    help="decode workload (the metric is quoted on llama3_8b_decode)")
+    ap.add_argument("--variant", default=None,
+                    help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "
+                         "a 2 GiB + 4 MiB cache")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -165,7 +170,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
         return
-    w = make_workload("llama3_8b_decode", device="cuda", variant=args.variant)
+    w = make_workload(args.workload, device="cuda", variant=args.variant)
     shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
     splits = pa.resolve_num_splits(shape, args.splits)
     ws_bytes = pa.workspace_bytes(shape, args.splits)
@@ -191,6 +196,7 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
 
     nbytes = kv_bytes(w)
+    spec = w.spec
     gbps = nbytes / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -205,13 +211,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": spec.dtype,
         "data": "synthetic: seeded N(0,1) q/k/v, seeded random page permutation",
         "config": {
-            "workload": "llama3_8b_decode: B=256 Hq=32 Hkv=8 D=128 bf16 page16 Skv=4096, "
-                        "K and V caches 2 GiB each (65,536 pages)",
-            "batch": w.q.shape[0], "seq_kv": 4096, "num_q_heads": 32, "num_kv_heads": 8,
-            "head_dim": 128, "page_size": 16, "num_splits": splits,
+            "workload": f"{spec.name}: {spec.description}, "
+                        f"{w.k_cache.shape[0]:,} pages per cache tensor",
+            "batch": w.q.shape[0], "seq_kv": max(w.seq_lens_host),
+            "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim, "page_size": spec.page_size, "num_splits": splits,
             "page_order": args.variant or "random",
             "kv_bytes_per_step": nbytes,
         },
@@ -221,7 +228,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic() if splits == 1 else None,
+            "traffic": measured_traffic() if (splits == 1 and spec.name == "llama3_8b_decode"
+                                              and not args.variant) else None,
         },
     }
     if splits > 1:

@@ -6,21 +6,29 @@
 
 namespace pa {
 
-constexpr int kValuWaves = 4;
+template <typename T, int D, int PS, int MR>
+hipError_t launch_attn_valu_cfg(const AttnParams& p, const AttnPlan& plan, int batch,
+                                hipStream_t stream) {
+  constexpr ValuConfig cfg = valu_config(sizeof(T), D, PS, MR);
+  if (plan.waves != cfg.waves || cfg.waves % plan.heads_per_wg != 0 ||
+      p.num_kv_heads % plan.heads_per_wg != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads / plan.heads_per_wg, batch);
+  const dim3 block(cfg.waves * 64);
+  attn_valu_kernel<T, D, PS, MR, cfg.waves, cfg.pages_ahead, true><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
 
 template <typename T, int D, int PS>
 hipError_t launch_attn_valu_dp(const AttnParams& p, const AttnPlan& plan, int batch,
                                hipStream_t stream) {
-  const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads, batch);
-  const dim3 block(kValuWaves * 64);
   switch (plan.rows_per_wg) {
-    case 1: attn_valu_kernel<T, D, PS, 1, kValuWaves><<<grid, block, 0, stream>>>(p); break;
-    case 2: attn_valu_kernel<T, D, PS, 2, kValuWaves><<<grid, block, 0, stream>>>(p); break;
-    case 4: attn_valu_kernel<T, D, PS, 4, kValuWaves><<<grid, block, 0, stream>>>(p); break;
-    case 8: attn_valu_kernel<T, D, PS, 8, kValuWaves><<<grid, block, 0, stream>>>(p); break;
+    case 1: return launch_attn_valu_cfg<T, D, PS, 1>(p, plan, batch, stream);
+    case 2: return launch_attn_valu_cfg<T, D, PS, 2>(p, plan, batch, stream);
+    case 4: return launch_attn_valu_cfg<T, D, PS, 4>(p, plan, batch, stream);
+    case 8: return launch_attn_valu_cfg<T, D, PS, 8>(p, plan, batch, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <typename T>

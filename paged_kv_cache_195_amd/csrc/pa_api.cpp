@@ -12,9 +12,9 @@
 
 namespace {
 
-// Workgroups that keep every compute unit of an MI355X (256 CUs) busy with a
-// few resident workgroups each; the automatic split count aims at this.
-constexpr int64_t kTargetWorkgroups = 1024;
+// The automatic split count aims at this many resident waves: 16 per compute
+// unit on the 256 compute units of an MI355X.
+constexpr int64_t kTargetWaves = 256 * 16;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxAutoSplits = 64;
 constexpr size_t kAlign = 256;
@@ -59,7 +59,9 @@ int check_shape(const pa_shape* s, bool decode) {
   // Envelope of the compiled kernels (grid y = Hkv and z = B are 16-bit).
   if (s->batch > 65535 || s->num_kv_heads > 65535) return PA_EUNSUPPORTED;
   if (s->head_dim_qk != s->head_dim_v) return PA_EUNSUPPORTED;
-  if (!pa::attn_valu_supported(s->head_dim_qk, s->page_size)) return PA_EUNSUPPORTED;
+  if ((s->head_dim_qk != 32 && s->head_dim_qk != 64 && s->head_dim_qk != 128) ||
+      (s->page_size != 16 && s->page_size != 32))
+    return PA_EUNSUPPORTED;
   return PA_OK;
 }
 
@@ -69,11 +71,24 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
   plan.rows_per_wg = rows_per_wg(rows_per_kvh);
   plan.row_groups = static_cast<int>((rows_per_kvh + plan.rows_per_wg - 1) / plan.rows_per_wg);
+  const int elem = s->dtype == PA_F32 ? 4 : 2;
+  plan.waves = pa::valu_config(elem, s->head_dim_qk, s->page_size, plan.rows_per_wg).waves;
+  // kv heads per workgroup: the largest divisor of Hkv that also divides the
+  // wave count, at most 8 (a workgroup then reads most of each page it touches)
+  plan.heads_per_wg = 1;
+  for (int k = 8; k >= 1; k /= 2) {
+    if (plan.waves % k == 0 && s->num_kv_heads % k == 0) {
+      plan.heads_per_wg = k;
+      break;
+    }
+  }
   if (num_splits > 0) {
     plan.num_splits = num_splits;
   } else {
-    const int64_t units = static_cast<int64_t>(s->batch) * s->num_kv_heads * plan.row_groups;
-    int64_t want = (kTargetWorkgroups + units - 1) / units;
+    const int64_t units =
+        static_cast<int64_t>(s->batch) * (s->num_kv_heads / plan.heads_per_wg) * plan.row_groups;
+    const int64_t target = (kTargetWaves + plan.waves - 1) / plan.waves;
+    int64_t want = (target + units - 1) / units;
     if (want > s->max_pages_per_seq) want = s->max_pages_per_seq;
     if (want > kMaxAutoSplits) want = kMaxAutoSplits;
     plan.num_splits = want < 1 ? 1 : static_cast<int>(want);
@@ -137,6 +152,7 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
   p.rows_per_kvh = s->seq_q * group;
   p.num_splits = plan.num_splits;
   p.causal = causal ? 1 : 0;
+  p.heads_per_wg = plan.heads_per_wg;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -163,11 +179,6 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
 }
 
 }  // namespace
-
-bool pa::attn_valu_supported(int head_dim, int page_size) {
-  return (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
-         (page_size == 16 || page_size == 32);
-}
 
 extern "C" {
 

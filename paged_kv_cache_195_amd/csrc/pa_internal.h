@@ -26,15 +26,35 @@ struct AttnParams {
   int32_t rows_per_kvh;        // Sq * group: query rows that share one kv head
   int32_t num_splits;          // S >= 1
   int32_t causal;
+  int32_t heads_per_wg;        // kv heads one workgroup serves (divides Hkv and its wave count)
   float scale_log2;            // scale * log2(e): scores are kept in base 2
 };
 
 // Launch shape chosen on the host.
 struct AttnPlan {
-  int rows_per_wg;   // MR: query rows (position, head) one workgroup carries
+  int rows_per_wg;   // MR: query rows (position, head) per kv head in one workgroup
   int row_groups;    // ceil(rows_per_kvh / MR)
   int num_splits;    // S
+  int waves;         // waves per workgroup
+  int heads_per_wg;  // kv heads per workgroup
 };
+
+// Launch shape compiled for each (element bytes, D, page size, MR).  nl is the
+// number of 16-byte wave loads per page and per cache tensor.  Kernels whose
+// working set fits 128 VGPRs run 16 waves (one 1024-thread workgroup fills a
+// compute unit) and rely on occupancy for loads in flight; larger ones run 8
+// waves.  Measured on the Llama-3-8B decode shape, a deeper per-wave register
+// ring (pages_ahead > 0) gained nothing over occupancy and pushed the larger
+// kernels into spills, so every configuration streams one page at a time.
+struct ValuConfig {
+  int waves;
+  int pages_ahead;
+};
+
+constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, int rows_per_wg) {
+  return (page_size * head_dim * elem_bytes / 1024 <= 4 && rows_per_wg <= 4) ? ValuConfig{16, 0}
+                                                                              : ValuConfig{8, 0};
+}
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
@@ -46,8 +66,6 @@ hipError_t launch_attn_valu_f16(const AttnParams& p, const AttnPlan& plan, int h
 hipError_t launch_attn_valu_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
                                  int page_size, int batch, hipStream_t stream);
 
-// True when the (head_dim, page_size) pair has a compiled kernel.
-bool attn_valu_supported(int head_dim, int page_size);
 
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,

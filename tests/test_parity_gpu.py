@@ -265,3 +265,18 @@ def test_qwen3_235b_decode_straddles_2gib():
     say("qwen3_235b_decode straddle variant (pages past 2^31 bytes)")
     w, ids = _full_size("qwen3_235b_decode", variant="straddle")
     assert w.notes["max_used_page_start_bytes"] >= 2 ** 31
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+def test_scale_values(scale):
+    """Zero scale (uniform weights), a negative scale, a large scale."""
+    say(f"scale={scale}")
+    w = make_custom("bf16", [5, 40, 300], 8, 2, 128, 16, seed=17, device=DEV)
+    for splits in (1, 3):
+        out, lse = pa.decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, scale,
+                             num_splits=splits)
+        torch.cuda.synchronize()
+        xo, xl = O.attention(host(w.q), host(w.k_cache), host(w.v_cache), w.table_host.numpy(),
+                             np.array(w.seq_lens_host), scale, False)
+        assert_close(out, xo, torch.bfloat16, f"out S={splits}")
+        assert_close(lse, xl, torch.float32, f"lse S={splits}")
