@@ -28,6 +28,8 @@ SOURCES = [
     "attn_valu_f32.hip",
     "attn_valu_f16.hip",
     "attn_valu_bf16.hip",
+    "attn_mfma_f16.hip",
+    "attn_mfma_bf16.hip",
     "combine.hip",
 ]
 

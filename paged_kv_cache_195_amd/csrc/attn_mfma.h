@@ -1,0 +1,405 @@
+// Split-KV paged attention on the matrix cores (gfx950 MFMA), for 16-bit
+// caches when one kv head carries at least 8 query rows (grouped-query decode
+// with G >= 8, or prefill rows).
+//
+// A wave owns 16 query rows of one kv head (a row is a (query position, head
+// of the group) pair) and streams its kv head's pages in 16-token tiles:
+//
+//   S^T[16 tokens x 16 rows] = K_tile[16 x D] . Q^T[D x 16]
+//       D/32 v_mfma_f32_16x16x32 steps; K is the A operand (lane l: token
+//       l%16, 8 dims), Q^T the B operand, loaded once.
+//   O[16 rows x D] += P[16 x 16 tokens] . V_tile[16 x D]
+//       D/16 v_mfma_f32_16x16x16 blocks.  The S^T accumulator layout (lane l
+//       holds row l%16, tokens 4*(l/16)..+3) is exactly the A-operand layout
+//       of this product, so P needs no data movement.  V is read back from
+//       LDS with ds_read_b64_tr_b16, which returns four consecutive tokens of
+//       one dimension per lane: the B-operand layout.
+//
+// K and V tiles are loaded from HBM as whole rows (each wave load covers
+// 512/D full rows of D*2 bytes, the pattern that streams fastest) and staged
+// in the wave's own LDS rows; the operand layouts are read from there.  Inside
+// a row, 16-byte chunk c sits at position c ^ (2 r mod chunks), an XOR swizzle
+// that keeps the row writes, the K operand reads and the transposing V reads
+// free of bank conflicts.
+//
+// P is split into a high and a low 16-bit part (P = P_hi + P_lo, both fed to
+// the MFMA), so the weights keep about 16 significant bits instead of the 8
+// of a single bfloat16 rounding.
+//
+// Softmax state per row: ref (reference max of scaled scores, -inf before the
+// first valid key), msub (ref, or 0 while ref is -inf, so -inf - (-inf) never
+// forms), l (sum of weights, per lane over its tokens) and the O accumulator,
+// relative to msub.  ref is raised only when a tile's max exceeds it by more
+// than kSlack (log2 units) -- a wave-uniform branch -- so the rescale of O is
+// rare.  Guards and split ranges follow rocMLIR "Fix split-kv attention
+// masking and sweep RMS" (Technical Details): fully masked splits contribute
+// nothing and a zero row sum stores (0, -inf).  V rows of tokens past the
+// sequence length are zeroed in LDS, so NaN in a last page's tail never meets
+// a zero weight in the MFMA.
+#pragma once
+
+#include "device_common.h"
+#include "pa_internal.h"
+#include "page_table.h"
+
+namespace pa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16_t> {
+  // acc += A[16x32] . B[32x16]; operands are 8 packed bf16 (one u32x4)
+  static __device__ __forceinline__ f32x4 k32(const u32x4& a, const u32x4& b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  // acc += A[16x16] . B[16x16]; operands are 4 packed bf16
+  static __device__ __forceinline__ f32x4 k16(s16x4 a, s16x4 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+  }
+  // round to bf16 (nearest even) and back; x is finite and >= 0
+  static __device__ __forceinline__ uint32_t round_bits(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  }
+  static __device__ __forceinline__ float bits_to_float(uint32_t h) {
+    return __builtin_bit_cast(float, h << 16);
+  }
+};
+
+template <>
+struct Mfma<f16_t> {
+  static __device__ __forceinline__ f32x4 k32(const u32x4& a, const u32x4& b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 k16(s16x4 a, s16x4 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<f16_t>(x));
+  }
+  static __device__ __forceinline__ float bits_to_float(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(f16_t, static_cast<uint16_t>(h)));
+  }
+};
+
+// T: bf16_t or f16_t; D: head dim (= Dv, a multiple of 32); PS: tokens per
+// page (a multiple of 16); NW: waves per workgroup.  p.heads_per_wg kv heads
+// per workgroup, NW / heads_per_wg waves per head; each workgroup covers 16
+// rows per kv head (row group rg = blockIdx.x / S).
+template <typename T, int D, int PS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) {
+  static_assert(D % 32 == 0 && PS % 16 == 0, "tile shape");
+  constexpr int kKSteps = D / 32;         // 16x16x32 steps for q.k
+  constexpr int kNBlocks = D / 16;        // 16-dim output blocks
+  constexpr int kTiles = PS / 16;         // 16-token tiles per page
+  constexpr int kRowBytes = D * 2;
+  constexpr float kSlack = 8.f;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;   // 16-lane group
+  const int li = lane & 15;  // index inside the group
+
+  const int S = p.num_splits;
+  const int split = blockIdx.x % S;
+  const int rg = blockIdx.x / S;
+  const int kpw = p.heads_per_wg;
+  const int wph = NW / kpw;
+  const int kg = wave / wph;
+  const int sub = wave - kg * wph;
+  const int kvh = blockIdx.y * kpw + kg;
+  const int b = blockIdx.z;
+  const int Hkv = p.num_kv_heads;
+  const int G = p.group;
+  const int Sq = p.seq_q;
+  const int Hq = p.num_q_heads;
+
+  const int seq_len = p.seq_lens[b];
+  const int n_pages = (seq_len + PS - 1) / PS;
+
+  // ---- this lane's row (row li of the 16) and the key limits of the group
+  auto row_limit = [&](int r_lin) {
+    const int i = r_lin / G;
+    int l = seq_len;
+    if (p.causal) {
+      l = seq_len - Sq + i + 1;
+      l = l < 0 ? 0 : (l > seq_len ? seq_len : l);
+    }
+    return l;
+  };
+  const int my_r = rg * 16 + li;
+  const bool my_valid = my_r < p.rows_per_kvh;
+  // rows 0..15 of this group: limits are the same for every kv head
+  int max_lim = 0, min_lim = 0x7fffffff;
+  for (int r = 0; r < 16; ++r) {
+    const int r_lin = rg * 16 + r;
+    if (r_lin >= p.rows_per_kvh) break;
+    const int l = row_limit(r_lin);
+    max_lim = l > max_lim ? l : max_lim;
+    min_lim = l < min_lim ? l : min_lim;
+  }
+  const int my_lim = my_valid ? row_limit(my_r) : max_lim;
+
+  // Q^T as the B operand: lane l holds q[row li][32 s + 8 g .. +8]
+  u32x4 qb[kKSteps];
+  {
+    const int i = my_r / G;
+    const int h = kvh * G + (my_r - i * G);
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) qb[s] = u32x4{0u, 0u, 0u, 0u};
+    if (my_valid) {  // padding rows past the last row never touch q
+      const T* qrow =
+          static_cast<const T*>(p.q) + (static_cast<int64_t>(b * Sq + i) * Hq + h) * D;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) qb[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+    }
+  }
+  const float c = __builtin_fmaxf(__builtin_fabsf(p.scale_log2), 1.17549435e-38f);
+  if (p.scale_log2 < 0.f) {
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) qb[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+
+  // ---- split range (ceil-divided, clamped, cut at the last visible page)
+  const int per = (n_pages + S - 1) / S;
+  const int first = min(split * per, n_pages);
+  int end = min(first + per, n_pages);
+  end = min(end, (max_lim + PS - 1) / PS);
+
+  PageTable pt;
+  pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kRowBytes;
+  pt.n_pages = n_pages;
+
+  // Whole-row loads: wave load j covers rows j * kRowsPerLoad .. +kRowsPerLoad
+  // of the tile; lane l takes 16-byte chunk lc of row lr.
+  constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  constexpr int kRowsPerLoad = 64 / kChunks;   // rows per wave load
+  constexpr int kLoads = 16 / kRowsPerLoad;    // wave loads per tile (= kKSteps)
+  static_assert(kLoads == kKSteps, "one wave load per k-step");
+  const int lr = lane / kChunks;
+  const int lc = lane % kChunks;
+  const uint32_t lane_off = static_cast<uint32_t>((lr * Hkv + kvh) * kRowBytes + 16 * lc);
+  const uint32_t load_step = static_cast<uint32_t>(kRowsPerLoad * Hkv * kRowBytes);
+  const uint32_t tile_step = static_cast<uint32_t>(16 * Hkv * kRowBytes);
+  const char* kbase = static_cast<const char*>(p.k);
+  const char* vbase = static_cast<const char*>(p.v);
+
+  // LDS: per wave, a K tile and a V tile of 16 swizzled rows; reused for the
+  // final merge
+  constexpr int kTileLds = 2 * 16 * kRowBytes;
+  constexpr int kMergeLds = 16 * D * 4 + 2 * 16 * 4;
+  constexpr int kPerWave = kTileLds > kMergeLds ? kTileLds : kMergeLds;
+  __shared__ __attribute__((aligned(16))) char smem[NW * kPerWave];
+  char* my_lds = smem + wave * kPerWave;
+  lds_char* my_lds3 = (lds_char*)(smem) + wave * kPerWave;
+  char* lds_k = my_lds;
+  char* lds_v = my_lds + 16 * kRowBytes;
+  lds_char* lds_v3 = my_lds3 + 16 * kRowBytes;
+  // byte offset in a tile of 16-byte chunk c of row r
+  auto swz = [](int r, int c) { return r * kRowBytes + 16 * (c ^ ((2 * r) & (kChunks - 1))); };
+
+  float ref = kNegInf, msub = 0.f, lsum = 0.f;
+  f32x4 o[kNBlocks];
+#pragma unroll
+  for (int nb = 0; nb < kNBlocks; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_tile = [&](int64_t base, int t, u32x4* kk, u32x4* vv) {
+    const uint32_t off = lane_off + t * tile_step;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+      kk[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kbase + base + off + j * load_step));
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+      vv[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vbase + base + off + j * load_step));
+  };
+
+  auto consume_tile = [&](int tok0, const u32x4* kk, u32x4* vv) {
+    // stage K and V rows; V rows of tokens past the sequence become zero
+    const bool tail = tok0 + 16 > min_lim;  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int r = j * kRowsPerLoad + lr;
+      *reinterpret_cast<u32x4*>(lds_k + swz(r, lc)) = kk[j];
+      u32x4 vrow = vv[j];
+      if (tail && tok0 + r >= seq_len) vrow = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(lds_v + swz(r, lc)) = vrow;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // S^T: lane holds S[row li][token tok0 + 4 g + e]
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(lds_k + swz(li, 4 * s + g));
+      sacc = Mfma<T>::k32(ka, qb[s], sacc);
+    }
+    float x[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = tok0 + 4 * g + e < my_lim ? x[e] : kNegInf;
+    }
+
+    float tmax = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
+    const bool raise = tmax * c > ref + kSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+      float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
+      rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));  // max of row li over the tile
+      const float nref = __builtin_fmaxf(ref, rmax * c);
+      const float nsub = nref == kNegInf ? 0.f : nref;
+      const float alpha = fast_exp2(msub - nsub);
+      ref = nref;
+      msub = nsub;
+      lsum *= alpha;
+      // O rows 4 g + e need the factor of those rows, held by lanes 4 g + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+        for (int nb = 0; nb < kNBlocks; ++nb) o[nb][e] *= ae;
+      }
+    }
+
+    // weights, split into high and low 16-bit parts
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = fast_exp2(__builtin_fmaf(x[e], c, -msub));  // x = -inf gives 0
+      lsum += pe;
+      hi[e] = Mfma<T>::round_bits(pe);
+      lo[e] = Mfma<T>::round_bits(pe - Mfma<T>::bits_to_float(hi[e]));
+    }
+    const s16x4 phi = __builtin_bit_cast(
+        s16x4, uint64_t(hi[0] | (hi[1] << 16)) | (uint64_t(hi[2] | (hi[3] << 16)) << 32));
+    const s16x4 plo = __builtin_bit_cast(
+        s16x4, uint64_t(lo[0] | (lo[1] << 16)) | (uint64_t(lo[2] | (lo[3] << 16)) << 32));
+
+    // B operand for block nb: tokens 4 g .. 4 g + 3 of dimension 16 nb + li;
+    // source lane li points at row 4 g + li / 4, dimensions 16 nb + 4 (li % 4) ..
+    const int tr_row = 4 * g + (li >> 2);
+#pragma unroll
+    for (int nb = 0; nb < kNBlocks; ++nb) {
+      const int chunk = 2 * nb + ((li & 3) >> 1);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(lds_v3 + swz(tr_row, chunk) + 8 * (li & 1)));
+      o[nb] = Mfma<T>::k16(phi, vb, o[nb]);
+      o[nb] = Mfma<T>::k16(plo, vb, o[nb]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- stream: the wave takes pages first + sub, first + sub + wph, ...;
+  // each page is kTiles tiles; the next tile's loads are issued before the
+  // current tile is computed.
+  int slot = first + sub;
+  if (slot < end) {
+    int64_t base = pt.base(slot);
+    u32x4 kc[kKSteps], vc[kKSteps];
+    int t = 0;
+    load_tile(base, 0, kc, vc);
+    while (true) {
+      const int tok0 = slot * PS + 16 * t;
+      int nslot = slot, nt = t + 1;
+      if (nt == kTiles) {
+        nslot = slot + wph;
+        nt = 0;
+      }
+      const bool more = nslot < end;
+      int64_t nbase = base;
+      u32x4 kn[kKSteps], vn[kKSteps];
+      if (more) {
+        if (nslot != slot) nbase = pt.base(nslot);
+        load_tile(nbase, nt, kn, vn);
+      }
+      consume_tile(tok0, kc, vc);
+      if (!more) break;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        kc[s] = kn[s];
+        vc[s] = vn[s];
+      }
+      slot = nslot;
+      t = nt;
+      base = nbase;
+    }
+  }
+
+  // ---- finish this wave: row sums over the four token groups
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+
+  // ---- merge the waves of each kv head through LDS, then write
+  __syncthreads();  // every wave is done with its V tiles
+  float* mo = reinterpret_cast<float*>(my_lds);  // [16 rows][D]
+  float* mref = mo + 16 * D;                     // [16]
+  float* ml = mref + 16;                         // [16]
+#pragma unroll
+  for (int nb = 0; nb < kNBlocks; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mo[(4 * g + e) * D + 16 * nb + li] = o[nb][e];
+  if (g == 0) {
+    mref[li] = ref;
+    ml[li] = lsum;
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < kpw * 16 * D; idx += NW * 64) {
+    const int hg = idx / (16 * D);
+    const int r = (idx / D) % 16;
+    const int d = idx % D;
+    const int r_lin = rg * 16 + r;
+    if (r_lin >= p.rows_per_kvh) continue;
+    const int i = r_lin / G;
+    const int rid = (b * Sq + i) * Hq + (blockIdx.y * kpw + hg) * G + (r_lin - i * G);
+    float mx = kNegInf;
+    for (int w = hg * wph; w < (hg + 1) * wph; ++w)
+      mx = __builtin_fmaxf(mx, reinterpret_cast<const float*>(smem + w * kPerWave)[16 * D + r]);
+    const float wsub = mx == kNegInf ? 0.f : mx;
+    float tot = 0.f, a = 0.f;
+    for (int w = hg * wph; w < (hg + 1) * wph; ++w) {
+      const float* wo = reinterpret_cast<const float*>(smem + w * kPerWave);
+      const float wr = wo[16 * D + r];
+      // a wave with no valid key for this row has ref = -inf and l = 0, o = 0
+      const float f = wr == kNegInf ? 0.f : fast_exp2(wr - wsub);
+      tot += f * wo[16 * D + 16 + r];
+      a += f * wo[r * D + d];
+    }
+    float out, lse;
+    if (tot > 0.f) {
+      out = a / tot;
+      lse = (mx + log2f(tot)) * kLn2;
+    } else {
+      out = 0.f;
+      lse = kNegInf;
+    }
+    if (S == 1) {
+      static_cast<T*>(p.out)[static_cast<int64_t>(rid) * D + d] = from_float<T>(out);
+      if (d == 0 && p.lse != nullptr) p.lse[rid] = lse;
+    } else {
+      const int64_t prow = static_cast<int64_t>(rid) * S + split;
+      p.part_out[prow * D + d] = out;
+      if (d == 0) p.part_lse[prow] = lse;
+    }
+  }
+}
+
+}  // namespace pa

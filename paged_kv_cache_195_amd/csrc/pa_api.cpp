@@ -12,9 +12,9 @@
 
 namespace {
 
-// The automatic split count aims at this many resident waves: 16 per compute
-// unit on the 256 compute units of an MI355X.
-constexpr int64_t kTargetWaves = 256 * 16;
+// The automatic split count aims at one workgroup per compute unit of an
+// MI355X (256 CUs); every launch shape runs 8 or 16 waves per workgroup.
+constexpr int64_t kTargetWorkgroups = 256;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxAutoSplits = 64;
 constexpr size_t kAlign = 256;
@@ -69,10 +69,16 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   pa::AttnPlan plan;
   const int group = s->num_q_heads / s->num_kv_heads;
   const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
-  plan.rows_per_wg = rows_per_wg(rows_per_kvh);
-  plan.row_groups = static_cast<int>((rows_per_kvh + plan.rows_per_wg - 1) / plan.rows_per_wg);
   const int elem = s->dtype == PA_F32 ? 4 : 2;
-  plan.waves = pa::valu_config(elem, s->head_dim_qk, s->page_size, plan.rows_per_wg).waves;
+  plan.mfma = s->dtype != PA_F32 && rows_per_kvh >= pa::kMfmaMinRows;
+  if (plan.mfma) {
+    plan.rows_per_wg = 16;
+    plan.waves = pa::kMfmaWaves;
+  } else {
+    plan.rows_per_wg = rows_per_wg(rows_per_kvh);
+    plan.waves = pa::valu_config(elem, s->head_dim_qk, s->page_size, plan.rows_per_wg).waves;
+  }
+  plan.row_groups = static_cast<int>((rows_per_kvh + plan.rows_per_wg - 1) / plan.rows_per_wg);
   // kv heads per workgroup: the largest divisor of Hkv that also divides the
   // wave count, at most 8 (a workgroup then reads most of each page it touches)
   plan.heads_per_wg = 1;
@@ -87,8 +93,7 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   } else {
     const int64_t units =
         static_cast<int64_t>(s->batch) * (s->num_kv_heads / plan.heads_per_wg) * plan.row_groups;
-    const int64_t target = (kTargetWaves + plan.waves - 1) / plan.waves;
-    int64_t want = (target + units - 1) / units;
+    int64_t want = (kTargetWorkgroups + units - 1) / units;
     if (want > s->max_pages_per_seq) want = s->max_pages_per_seq;
     if (want > kMaxAutoSplits) want = kMaxAutoSplits;
     plan.num_splits = want < 1 ? 1 : static_cast<int>(want);
@@ -157,16 +162,22 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t err;
-  switch (s->dtype) {
-    case PA_F32:
-      err = pa::launch_attn_valu_f32(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-      break;
-    case PA_F16:
-      err = pa::launch_attn_valu_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-      break;
-    default:
-      err = pa::launch_attn_valu_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-      break;
+  if (plan.mfma) {
+    err = s->dtype == PA_F16
+              ? pa::launch_attn_mfma_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs)
+              : pa::launch_attn_mfma_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+  } else {
+    switch (s->dtype) {
+      case PA_F32:
+        err = pa::launch_attn_valu_f32(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+        break;
+      case PA_F16:
+        err = pa::launch_attn_valu_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+        break;
+      default:
+        err = pa::launch_attn_valu_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
+        break;
+    }
   }
   if (err != hipSuccess) return PA_EHIP;
   if (plan.num_splits > 1) {

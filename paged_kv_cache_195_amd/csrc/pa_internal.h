@@ -32,6 +32,7 @@ struct AttnParams {
 
 // Launch shape chosen on the host.
 struct AttnPlan {
+  bool mfma;         // matrix-core kernel (16-bit caches, >= 8 rows per kv head)
   int rows_per_wg;   // MR: query rows (position, head) per kv head in one workgroup
   int row_groups;    // ceil(rows_per_kvh / MR)
   int num_splits;    // S
@@ -56,6 +57,10 @@ constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, in
                                                                               : ValuConfig{8, 0};
 }
 
+// The matrix-core kernel: 16 rows per kv head and workgroup, 8 waves.
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaMinRows = 8;
+
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Grid = (S * row_groups, Hkv, B); returns a hipError_t.
@@ -66,6 +71,11 @@ hipError_t launch_attn_valu_f16(const AttnParams& p, const AttnPlan& plan, int h
 hipError_t launch_attn_valu_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
                                  int page_size, int batch, hipStream_t stream);
 
+
+hipError_t launch_attn_mfma_f16(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                int page_size, int batch, hipStream_t stream);
+hipError_t launch_attn_mfma_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                 int page_size, int batch, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,
