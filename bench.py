@@ -29,7 +29,10 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_traffic.md")
+TRAFFIC_FILES = {
+    "llama3_8b_decode": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_traffic.md"),
+    "qwen3_235b_decode": os.path.join(ROOT, "profiles", "attn_decode_qwen3_235b_traffic.md"),
+}
 KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
 
 
@@ -42,12 +45,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload: str = "llama3_8b_decode"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(workload)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     fields = dict(re.findall(r"^\s*[-*]?\s*`?(\w+)`?\s*[:=]\s*`?([0-9a-f.e+]+)`?\s*$", text, re.M))
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
@@ -228,8 +232,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic() if (splits == 1 and spec.name == "llama3_8b_decode"
-                                              and not args.variant) else None,
+            "traffic": measured_traffic(spec.name) if (splits == 1 and not args.variant) else None,
         },
     }
     if splits > 1:
