@@ -149,7 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--splits", type=int, default=0, help="split-KV count (0 = automatic)")
     ap.add_argument("--workload", default="llama3_8b_decode",
-                    choices=["llama3_8b_decode", "qwen3_235b_decode", "ragged_bf16", "tiny_f32"],
+                    choices=["llama3_8b_decode", "qwen3_235b_decode", "llama3_70b_decode",
+                             "decode_b64_s8192_g8", "ragged_bf16", "tiny_f32"],
                     help="decode workload (the metric is quoted on llama3_8b_decode)")
     ap.add_argument("--variant", default=None,
                     help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "

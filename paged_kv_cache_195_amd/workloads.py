@@ -36,6 +36,10 @@ Workloads (``WORKLOADS``):
                     cache (131,072 pages of 16 KiB); variant ``straddle`` with
                     131,328 pages (2 GiB + 4 MiB) so used pages lie on both
                     sides of byte offset 2^31.
+``llama3_70b_decode`` B=256, Hq=64, Hkv=8, D=128, page 16, L=4096, 2 GiB per
+                    cache (65,536 pages of 32 KiB).
+``decode_b64_s8192_g8`` B=64, Hq=64, Hkv=8, D=128, page 16, L=8192, 1 GiB per
+                    cache (32,768 pages of 32 KiB).
 """
 
 from __future__ import annotations
@@ -81,6 +85,12 @@ WORKLOADS = {
     "qwen3_235b_decode": WorkloadSpec("qwen3_235b_decode", "bf16", 256, 1, 64, 4, 128, 16, False,
                                       (0,), 4,
                                       "Qwen3-235B-A22B decode bf16 B=256 Hq=64 Hkv=4 D=128 page16 Skv=8192"),
+    "llama3_70b_decode": WorkloadSpec("llama3_70b_decode", "bf16", 256, 1, 64, 8, 128, 16, False,
+                                      (0,), 5,
+                                      "Llama-3-70B decode bf16 B=256 Hq=64 Hkv=8 D=128 page16 Skv=4096"),
+    "decode_b64_s8192_g8": WorkloadSpec("decode_b64_s8192_g8", "bf16", 64, 1, 64, 8, 128, 16, False,
+                                        (0,), 6,
+                                        "decode bf16 B=64 Hq=64 Hkv=8 D=128 page16 Skv=8192"),
 }
 
 WORKLOAD_ORDER = ["tiny_f32", "prefill_f16", "ragged_bf16", "llama3_8b_decode", "qwen3_235b_decode"]
@@ -169,6 +179,14 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         lens = list(seq_lens) if seq_lens is not None else [8192] * b
         width = 512
         phys = 131328 if variant == "straddle" else (131072 if batch is None else max(1, b * 512))
+    elif name == "llama3_70b_decode":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [4096] * b
+        width, phys = 256, b * 256
+    elif name == "decode_b64_s8192_g8":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [8192] * b
+        width, phys = 512, b * 512
     else:
         raise KeyError(name)
 

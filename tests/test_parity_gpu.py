@@ -261,6 +261,16 @@ def test_qwen3_235b_decode_full_size_sampled():
     _full_size("qwen3_235b_decode")
 
 
+def test_llama3_70b_decode_full_size_sampled():
+    say("llama3_70b_decode full size (G=8), sampled parity")
+    _full_size("llama3_70b_decode")
+
+
+def test_decode_b64_s8192_g8_full_size_sampled():
+    say("decode_b64_s8192_g8 full size (G=8), sampled parity")
+    _full_size("decode_b64_s8192_g8", sample=(0, 17, 40, 63))
+
+
 def test_qwen3_235b_decode_straddles_2gib():
     say("qwen3_235b_decode straddle variant (pages past 2^31 bytes)")
     w, ids = _full_size("qwen3_235b_decode", variant="straddle")
