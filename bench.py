@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA peaks
 TRAFFIC_FILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_traffic.md"),
     "qwen3_235b_decode": os.path.join(ROOT, "profiles", "attn_decode_qwen3_235b_traffic.md"),
@@ -150,13 +151,16 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split-KV count (0 = automatic)")
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "qwen3_235b_decode", "llama3_70b_decode",
-                             "decode_b64_s8192_g8", "ragged_bf16", "tiny_f32"],
+                             "decode_b64_s8192_g8", "ragged_bf16", "tiny_f32",
+                             "prefill_b4_s1024", "prefill_b1_s4096", "prefill_f16"],
                     help="decode workload (the metric is quoted on llama3_8b_decode)")
     ap.add_argument("--variant", default=None,
                     help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "
                          "a 2 GiB + 4 MiB cache")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and replay it (no host launch cost)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -169,7 +173,7 @@ def main():
     import torch
 
     import paged_kv_cache_195_amd as pa
-    from paged_kv_cache_195_amd.workloads import kv_bytes, make_workload
+    from paged_kv_cache_195_amd.workloads import attention_flops, kv_bytes, make_workload
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -184,18 +188,41 @@ def main():
                       device="cuda")
     lse = torch.empty(out.shape[:3], dtype=torch.float32, device="cuda")
 
+    prefill = w.q.shape[1] > 1
+    if prefill:
+        out = torch.empty((w.q.shape[0], w.q.shape[1], w.q.shape[2], w.v_cache.shape[3]),
+                          dtype=w.q.dtype, device="cuda")
+        lse = torch.empty(out.shape[:3], dtype=torch.float32, device="cuda")
+
     def step():
-        pa.decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
-                  num_splits=args.splits, out=out, lse=lse, workspace=workspace)
+        fn = pa.prefill if prefill else pa.decode
+        fn(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale, causal=w.causal,
+           num_splits=args.splits, out=out, lse=lse, workspace=workspace)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -203,6 +230,23 @@ def main():
     nbytes = kv_bytes(w)
     spec = w.spec
     gbps = nbytes / (ms * 1e-3) / 1e9
+    if prefill:
+        flops = attention_flops(w)
+        tflops = flops / (ms * 1e-3) / 1e12
+        line = {
+            "metric": "paged causal prefill TFLOP/s (% of bf16 MFMA peak) + us/step",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": spec.dtype, "data": "synthetic: seeded N(0,1) q/k/v, seeded page permutation",
+            "config": {"workload": f"{spec.name}: {spec.description}", "num_splits": splits,
+                       "flops_per_step": flops, "graph": args.graph},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": MFMA_PEAK_TFLOPS[spec.dtype], "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_PEAK_TFLOPS[spec.dtype], 4), "traffic": None},
+        }
+        print(json.dumps(line), flush=True)
+        return
     line = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -226,6 +270,7 @@ def main():
             "head_dim": spec.head_dim, "page_size": spec.page_size, "num_splits": splits,
             "page_order": args.variant or "random",
             "kv_bytes_per_step": nbytes,
+            "graph": args.graph,
         },
         "roofline": {
             "bound": "hbm",

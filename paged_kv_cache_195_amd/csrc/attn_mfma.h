@@ -49,6 +49,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -66,14 +68,17 @@ struct Mfma<bf16_t> {
   static __device__ __forceinline__ f32x4 k16(s16x4 a, s16x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
   }
-  // round to bf16 (nearest even) and back; x is finite and >= 0
-  static __device__ __forceinline__ uint32_t round_bits(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  // Two weights a, b (finite, >= 0) as packed high and low parts:
+  // hi = the top 16 bits of each (exact as floats), lo = bf16(p - hi) rounded
+  // to nearest even, so hi + lo keeps about 16 significant bits.
+  static __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+    const f32x2 rest = {a - __builtin_bit_cast(float, ua & 0xffff0000u),
+                        b - __builtin_bit_cast(float, ub & 0xffff0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_v));
   }
-  static __device__ __forceinline__ float bits_to_float(uint32_t h) {
-    return __builtin_bit_cast(float, h << 16);
-  }
+  static constexpr uint32_t kOnes = 0x3f803f80u;  // two packed 1.0
 };
 
 template <>
@@ -86,12 +91,15 @@ struct Mfma<f16_t> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                  __builtin_bit_cast(f16x4_t, b), acc, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t round_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<f16_t>(x));
+  // hi = each weight rounded toward zero to f16, lo = the rest, also
+  // rounded toward zero (weights are at most 2^8, well inside f16 range).
+  static __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a - static_cast<float>(h[0]),
+                                                                 b - static_cast<float>(h[1])));
   }
-  static __device__ __forceinline__ float bits_to_float(uint32_t h) {
-    return static_cast<float>(__builtin_bit_cast(f16_t, static_cast<uint16_t>(h)));
-  }
+  static constexpr uint32_t kOnes = 0x3c003c00u;  // two packed 1.0
 };
 
 // T: bf16_t or f16_t; D: head dim (= Dv, a multiple of 32); PS: tokens per
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
   const int n_pages = (seq_len + PS - 1) / PS;
 
   // ---- this lane's row (row li of the 16) and the key limits of the group
-  auto row_limit = [&](int r_lin) {
+  auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
     const int i = r_lin / G;
     int l = seq_len;
     if (p.causal) {
@@ -209,14 +217,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
   char* lds_v = my_lds + 16 * kRowBytes;
   lds_char* lds_v3 = my_lds3 + 16 * kRowBytes;
   // byte offset in a tile of 16-byte chunk c of row r
-  auto swz = [](int r, int c) { return r * kRowBytes + 16 * (c ^ ((2 * r) & (kChunks - 1))); };
+  auto swz = [](int r, int c) __attribute__((always_inline)) { return r * kRowBytes + 16 * (c ^ ((2 * r) & (kChunks - 1))); };
 
   float ref = kNegInf, msub = 0.f, lsum = 0.f;
   f32x4 o[kNBlocks];
 #pragma unroll
   for (int nb = 0; nb < kNBlocks; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_tile = [&](int64_t base, int t, u32x4* kk, u32x4* vv) {
+  auto load_tile = [&](int64_t base, int t, u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
     const uint32_t off = lane_off + t * tile_step;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j)
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
           reinterpret_cast<const u32x4*>(vbase + base + off + j * load_step));
   };
 
-  auto consume_tile = [&](int tok0, const u32x4* kk, u32x4* vv) {
+  auto consume_tile = [&](int tok0, const u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
     // stage K and V rows; V rows of tokens past the sequence become zero
     const bool tail = tok0 + 16 > min_lim;  // wave-uniform
 #pragma unroll
@@ -278,18 +286,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
     }
 
     // weights, split into high and low 16-bit parts
-    uint32_t hi[4], lo[4];
+    float pe[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pe = fast_exp2(__builtin_fmaf(x[e], c, -msub));  // x = -inf gives 0
-      lsum += pe;
-      hi[e] = Mfma<T>::round_bits(pe);
-      lo[e] = Mfma<T>::round_bits(pe - Mfma<T>::bits_to_float(hi[e]));
+      pe[e] = fast_exp2(__builtin_fmaf(x[e], c, -msub));  // x = -inf gives 0
+      lsum += pe[e];
     }
-    const s16x4 phi = __builtin_bit_cast(
-        s16x4, uint64_t(hi[0] | (hi[1] << 16)) | (uint64_t(hi[2] | (hi[3] << 16)) << 32));
-    const s16x4 plo = __builtin_bit_cast(
-        s16x4, uint64_t(lo[0] | (lo[1] << 16)) | (uint64_t(lo[2] | (lo[3] << 16)) << 32));
+    uint32_t h01, l01, h23, l23;
+    Mfma<T>::split2(pe[0], pe[1], h01, l01);
+    Mfma<T>::split2(pe[2], pe[3], h23, l23);
+    const s16x4 phi = __builtin_bit_cast(s16x4, uint64_t(h01) | (uint64_t(h23) << 32));
+    const s16x4 plo = __builtin_bit_cast(s16x4, uint64_t(l01) | (uint64_t(l23) << 32));
 
     // B operand for block nb: tokens 4 g .. 4 g + 3 of dimension 16 nb + li;
     // source lane li points at row 4 g + li / 4, dimensions 16 nb + 4 (li % 4) ..

@@ -1,0 +1,355 @@
+// Paged prefill attention on the matrix cores (gfx950 MFMA), for 16-bit
+// caches when one kv head carries many query rows (a row is a (query
+// position, head of the group) pair).
+//
+// A workgroup owns 16 * RB * NW rows of one kv head; wave w owns RB blocks of
+// 16 rows.  The workgroup walks its split's keys in 64-token tiles.  Each
+// tile of K and V is loaded once, cooperatively (every wave loads whole rows
+// of it with global_load_lds_dwordx4, straight into LDS, no registers), into
+// one of two LDS buffers, and every wave computes its rows against it, so
+// each K/V byte read from memory serves 16 * RB * NW rows and each operand
+// read from LDS serves RB row blocks.  The next tile's loads are issued
+// before the current tile is computed.
+//
+// Per 16-token sub-tile and row block, S^T = K . Q^T is the decode MFMA
+// kernel's product (v_mfma_f32_16x16x32, K from LDS, Q^T in registers); its
+// accumulator holds, per lane, row l%16 and tokens 4*(l/16)..+3.  O += P . V
+// runs on 32-token halves with v_mfma_f32_16x16x32 as well: the order of the
+// 32 tokens along K is free as long as both operands agree, so lane l's eight
+// A values are its four weights from each of the two sub-tiles, and its
+// eight B values are the two transposing LDS reads (ds_read_b64_tr_b16) of
+// those sub-tiles -- no data moves between lanes.  P is split into high and
+// low 16-bit parts.  LDS rows use the same XOR swizzle as the decode kernel.
+//
+// Causal masking is bottom-right (row i of Sq sits at key position
+// L - Sq + i); tiles past the last key any row of the workgroup can see are
+// skipped.  The running state, the guards against -inf - (-inf) and 0/0, and
+// the split ranges follow rocMLIR "Fix split-kv attention masking and sweep
+// RMS" (Technical Details), as in the decode kernels.  Every wave owns
+// distinct rows, so no cross-wave merge is needed.
+#pragma once
+
+#include "attn_mfma.h"
+
+namespace pa {
+
+template <typename T, int D, int PS, int NW, int RB>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const AttnParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(PS == 16 || PS == 32, "page size");
+  constexpr int kTile = 64;                      // tokens per tile
+  constexpr int kSub = kTile / 16;               // 16-token sub-tiles
+  constexpr int kKSteps = D / 32;
+  constexpr int kNBlocks = D / 16;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  constexpr int kRowsPerLoad = 64 / kChunks;     // rows per wave load
+  constexpr int kRowsPerWave = kTile / NW;       // tile rows each wave loads
+  constexpr int kLoads = kRowsPerWave / kRowsPerLoad;
+  static_assert(kRowsPerWave % kRowsPerLoad == 0 && kLoads >= 1, "load split");
+  static_assert(kRowsPerWave <= PS, "a wave's rows stay inside one page");
+  constexpr int kRowsPerWaveQ = 16 * RB;         // query rows per wave
+  constexpr int kBuf = kTile * kRowBytes;        // one K or V tile in LDS
+  constexpr float kSlack = 8.f;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  const int S = p.num_splits;
+  const int split = blockIdx.x % S;
+  // heaviest (latest) row groups first: they see the most keys
+  const int n_rg = gridDim.x / S;
+  const int rg = n_rg - 1 - static_cast<int>(blockIdx.x / S);
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Hkv = p.num_kv_heads;
+  const int G = p.group;
+  const int Sq = p.seq_q;
+  const int Hq = p.num_q_heads;
+
+  const int seq_len = p.seq_lens[b];
+  const int n_pages = (seq_len + PS - 1) / PS;
+
+  auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
+    const int i = r_lin / G;
+    int l = seq_len;
+    if (p.causal) {
+      l = seq_len - Sq + i + 1;
+      l = l < 0 ? 0 : (l > seq_len ? seq_len : l);
+    }
+    return l;
+  };
+  // rows of the workgroup: [wg_first, +16 RB NW); the last one sees the most keys
+  const int wg_first = rg * kRowsPerWaveQ * NW;
+  const int wg_last = min(wg_first + kRowsPerWaveQ * NW, p.rows_per_kvh) - 1;
+  const int wg_max_lim = row_limit(wg_last);
+  // this wave's rows: [wave_first, +16 RB); block rb, lane row li is wave_first + 16 rb + li
+  const int wave_first = wg_first + kRowsPerWaveQ * wave;
+  const int wave_last = min(wave_first + kRowsPerWaveQ - 1, p.rows_per_kvh - 1);
+  const int wave_min_lim = row_limit(min(wave_first, p.rows_per_kvh - 1));
+  const int wave_max_lim = wave_first < p.rows_per_kvh ? row_limit(wave_last) : 0;
+  int my_lim[RB];
+  u32x4 qb[RB][kKSteps];
+  const float c = __builtin_fmaxf(__builtin_fabsf(p.scale_log2), 1.17549435e-38f);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wave_first + 16 * rb + li;
+    const bool valid = r < p.rows_per_kvh;
+    my_lim[rb] = valid ? row_limit(r) : 0;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) qb[rb][s] = u32x4{0u, 0u, 0u, 0u};
+    if (valid) {
+      const int i = r / G;
+      const int h = kvh * G + (r - i * G);
+      const T* qrow = static_cast<const T*>(p.q) + (static_cast<int64_t>(b * Sq + i) * Hq + h) * D;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        qb[rb][s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+    }
+    if (p.scale_log2 < 0.f) {
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        qb[rb][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+  }
+
+  // ---- split range in pages, cut at the last page the workgroup can see
+  const int per = (n_pages + S - 1) / S;
+  const int first = min(split * per, n_pages);
+  int end = min(first + per, n_pages);
+  end = min(end, (wg_max_lim + PS - 1) / PS);
+  const int tok_begin = first * PS;
+  const int tok_end = min(end * PS, seq_len);  // keys of this split (and no further)
+
+  PageTable pt;
+  pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kRowBytes;
+  pt.n_pages = n_pages;
+
+  // ---- LDS: two K/V tile buffers (swizzled rows)
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kBuf];
+  lds_char* smem3 = (lds_char*)(smem);
+  auto swz = [](int r, int cidx) __attribute__((always_inline)) {
+    return r * kRowBytes + 16 * (cidx ^ ((2 * r) & (kChunks - 1)));
+  };
+
+  // this wave loads tile rows [kRowsPerWave * wave, +kRowsPerWave): lane l
+  // writes LDS position lc of row lr of each wave load (its place is fixed by
+  // the lane index), so it fetches the chunk that the swizzle puts there
+  const int lr = lane / kChunks;
+  const int lc = lane % kChunks;
+  const char* kbase = static_cast<const char*>(p.k);
+  const char* vbase = static_cast<const char*>(p.v);
+  typedef __attribute__((address_space(1))) const void* global_ptr;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+
+  // Issue this wave's loads of a tile; returns true when some of its rows lie
+  // at or past tok_end (their V rows must then be zeroed once the loads land).
+  auto load_tile = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
+    const int row0 = kRowsPerWave * wave;                    // first tile row of this wave
+    const int tok = tile_tok0 + row0;
+    if (tok < tok_end) {                                     // wave-uniform
+      const int64_t base = pt.base(tok / PS);                // one page per wave
+      const int in_page = tok % PS;
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int r = row0 + j * kRowsPerLoad + lr;          // tile row of this lane
+        const int chunk = lc ^ ((2 * r) & (kChunks - 1));
+        const uint32_t off = static_cast<uint32_t>(
+            ((in_page + j * kRowsPerLoad + lr) * Hkv + kvh) * kRowBytes + 16 * chunk);
+        const int lds_off = buf * 2 * kBuf + (row0 + j * kRowsPerLoad) * kRowBytes;
+        __builtin_amdgcn_global_load_lds((global_ptr)(kbase + base + off),
+                                         (lds_ptr)(smem3 + lds_off), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_ptr)(vbase + base + off),
+                                         (lds_ptr)(smem3 + lds_off + kBuf), 16, 0, 0);
+      }
+    }
+    return tok + kRowsPerWave > tok_end;
+  };
+  // Zero this wave's V rows at or past tok_end (past the sequence end, in a
+  // page of the next split, or never loaded), after its loads have landed, so
+  // no garbage meets a zero weight in the MFMA.  K rows there are harmless:
+  // their scores are masked.
+  auto zero_tail = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads are in LDS
+    char* vb = smem + buf * 2 * kBuf + kBuf;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int r = kRowsPerWave * wave + j * kRowsPerLoad + lr;
+      if (tile_tok0 + r >= tok_end)
+        *reinterpret_cast<u32x4*>(vb + r * kRowBytes + 16 * lc) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // lsum[rb] accumulates P . 1 on the matrix cores: lane (g, li) holds the
+  // row sums of rows 4 g + e, the same rows as its output elements
+  float ref[RB], msub[RB];
+  f32x4 o[RB][kNBlocks], lsum[RB];
+  const u32x4 ones = {Mfma<T>::kOnes, Mfma<T>::kOnes, Mfma<T>::kOnes, Mfma<T>::kOnes};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    ref[rb] = kNegInf;
+    msub[rb] = 0.f;
+    lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One 32-token half of a tile: scores, lazy rescale, P . V.
+  auto compute_half = [&](const char* kb, lds_char* vb3, int h, int tile_tok0) __attribute__((always_inline)) {
+    // scores of row block rb, row li, tokens tile_tok0 + 32 h + 16 q2 + 4 g + e
+    float x[RB][2][4];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      f32x4 sacc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const u32x4 ka =
+            *reinterpret_cast<const u32x4*>(kb + swz(32 * h + 16 * q2 + li, 4 * s + g));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb] = Mfma<T>::k32(ka, qb[rb][s], sacc[rb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[rb][q2][e] = sacc[rb][e];
+    }
+    const int tok0 = tile_tok0 + 32 * h;
+    // mask keys a row may not see, or outside the split (wave-uniform test)
+    if (tok0 + 32 > wave_min_lim || tok0 + 32 > tok_end) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int lim = min(my_lim[rb], tok_end);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[rb][q2][e] = tok0 + 16 * q2 + 4 * g + e < lim ? x[rb][q2][e] : kNegInf;
+      }
+    }
+    // lazy rescale of each row block
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = __builtin_fmaxf(tmax, x[rb][q2][e]);
+      const bool raise = tmax * c > ref[rb] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+        float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
+        rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));
+        const float nref = __builtin_fmaxf(ref[rb], rmax * c);
+        const float nsub = nref == kNegInf ? 0.f : nref;
+        const float alpha = fast_exp2(msub[rb] - nsub);
+        ref[rb] = nref;
+        msub[rb] = nsub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __builtin_bit_cast(
+              float,
+              __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, alpha)));
+          lsum[rb][e] *= ae;
+#pragma unroll
+          for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb][e] *= ae;
+        }
+      }
+    }
+    // weights as 8 high and 8 low 16-bit values per row block; row sums on
+    // the matrix cores
+    u32x4 phi[RB], plo[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pe[8];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pe[4 * q2 + e] = fast_exp2(__builtin_fmaf(x[rb][q2][e], c, -msub[rb]));
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) Mfma<T>::split2(pe[2 * w], pe[2 * w + 1], hi[w], lo[w]);
+      phi[rb] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      plo[rb] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      lsum[rb] = Mfma<T>::k32(phi[rb], ones, lsum[rb]);
+      lsum[rb] = Mfma<T>::k32(plo[rb], ones, lsum[rb]);
+    }
+    const int tr_row = 4 * g + (li >> 2);
+#pragma unroll
+    for (int nb = 0; nb < kNBlocks; ++nb) {
+      const int chunk = 2 * nb + ((li & 3) >> 1);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vb3 + swz(32 * h + tr_row, chunk) + 8 * (li & 1)));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vb3 + swz(32 * h + 16 + tr_row, chunk) + 8 * (li & 1)));
+      const u32x4 vv =
+          __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        o[rb][nb] = Mfma<T>::k32(phi[rb], vv, o[rb][nb]);
+        o[rb][nb] = Mfma<T>::k32(plo[rb], vv, o[rb][nb]);
+      }
+    }
+  };
+  auto compute_tile = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
+    const char* kb = smem + buf * 2 * kBuf;
+    lds_char* vb3 = smem3 + buf * 2 * kBuf + kBuf;
+    compute_half(kb, vb3, 0, tile_tok0);
+    if (tile_tok0 + 32 < wave_max_lim) compute_half(kb, vb3, 1, tile_tok0);
+  };
+
+  // ---- tile loop (every wave of the workgroup runs every tile: the LDS
+  // buffers are shared, so the barriers must be reached by all of them)
+  const int n_tiles = tok_end > tok_begin ? (tok_end - tok_begin + kTile - 1) / kTile : 0;
+  if (n_tiles > 0) {
+    if (load_tile(0, tok_begin)) zero_tail(0, tok_begin);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int tok0 = tok_begin + t * kTile;
+    const bool more = t + 1 < n_tiles;
+    const bool tail = more && load_tile((t + 1) & 1, tok0 + kTile);
+    // a wave whose rows see none of this tile skips the arithmetic
+    if (tok0 < wave_max_lim) compute_tile(t & 1, tok0);
+    if (tail) zero_tail((t + 1) & 1, tok0 + kTile);
+    __syncthreads();  // the next tile has landed (the compiler waits for it) and this one is done
+  }
+
+  // ---- finish: normalize and write; row 4 g + e of the O layout has its sum
+  // in lsum[rb][e] and needs the reference of that row
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int src = (4 * g + e) << 2;
+      const float le = lsum[rb][e];
+      const float re = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, ref[rb])));
+      const int r_lin = wave_first + 16 * rb + 4 * g + e;
+      if (r_lin >= p.rows_per_kvh) continue;
+      const int i = r_lin / G;
+      const int rid = (b * Sq + i) * Hq + kvh * G + (r_lin - i * G);
+      const bool any = le > 0.f;  // no valid key: (0, -inf) instead of 0/0
+      const float lse = any ? (re + log2f(le)) * kLn2 : kNegInf;
+      if (S == 1) {
+        T* dst = static_cast<T*>(p.out) + static_cast<int64_t>(rid) * D;
+#pragma unroll
+        for (int nb = 0; nb < kNBlocks; ++nb)
+          dst[16 * nb + li] = from_float<T>(any ? o[rb][nb][e] / le : 0.f);
+        if (li == 0 && p.lse != nullptr) p.lse[rid] = lse;
+      } else {
+        const int64_t prow = static_cast<int64_t>(rid) * S + split;
+        float* dst = p.part_out + prow * D;
+#pragma unroll
+        for (int nb = 0; nb < kNBlocks; ++nb) dst[16 * nb + li] = any ? o[rb][nb][e] / le : 0.f;
+        if (li == 0) p.part_lse[prow] = lse;
+      }
+    }
+  }
+}
+
+}  // namespace pa

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void attn_valu_kernel(const AttnParams p) 
     for (int e = 0; e < kEpc; ++e) acc[r][e] = 0.f;
   }
 
-  auto load_page = [&](int slot, u32x4* kk, u32x4* vv) {
+  auto load_page = [&](int slot, u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
     const int64_t base = pt.base(slot);
 #pragma unroll
     for (int j = 0; j < kNl; ++j) {
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(NW * 64) void attn_valu_kernel(const AttnParams p) 
     }
   };
 
-  auto consume_page = [&](int slot, const u32x4* kk, u32x4* vv) {
+  auto consume_page = [&](int slot, const u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
     // unscaled scores q.k of this lane's tokens
     float x[kNl][MR];
 #pragma unroll

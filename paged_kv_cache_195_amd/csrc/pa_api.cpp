@@ -71,7 +71,12 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
   const int elem = s->dtype == PA_F32 ? 4 : 2;
   plan.mfma = s->dtype != PA_F32 && rows_per_kvh >= pa::kMfmaMinRows;
-  if (plan.mfma) {
+  plan.prefill = plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
+                 (s->head_dim_qk == 64 || s->head_dim_qk == 128);
+  if (plan.prefill) {
+    plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * pa::kPrefillWaves;
+    plan.waves = pa::kPrefillWaves;
+  } else if (plan.mfma) {
     plan.rows_per_wg = 16;
     plan.waves = pa::kMfmaWaves;
   } else {
@@ -82,7 +87,7 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   // kv heads per workgroup: the largest divisor of Hkv that also divides the
   // wave count, at most 8 (a workgroup then reads most of each page it touches)
   plan.heads_per_wg = 1;
-  for (int k = 8; k >= 1; k /= 2) {
+  for (int k = 8; k >= 1 && !plan.prefill; k /= 2) {
     if (plan.waves % k == 0 && s->num_kv_heads % k == 0) {
       plan.heads_per_wg = k;
       break;

@@ -33,6 +33,7 @@ struct AttnParams {
 // Launch shape chosen on the host.
 struct AttnPlan {
   bool mfma;         // matrix-core kernel (16-bit caches, >= 8 rows per kv head)
+  bool prefill;      // the shared-tile prefill variant of it (>= 64 rows per kv head)
   int rows_per_wg;   // MR: query rows (position, head) per kv head in one workgroup
   int row_groups;    // ceil(rows_per_kvh / MR)
   int num_splits;    // S
@@ -60,6 +61,11 @@ constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, in
 // The matrix-core kernel: 16 rows per kv head and workgroup, 8 waves.
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaMinRows = 8;
+// The shared-tile prefill kernel: kPrefillRowBlocks blocks of 16 rows per
+// wave, kPrefillWaves waves, one kv head per workgroup; D in {64, 128}.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowBlocks = 2;
+constexpr int kPrefillMinRows = 64;
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 

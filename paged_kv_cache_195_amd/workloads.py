@@ -40,6 +40,10 @@ Workloads (``WORKLOADS``):
                     cache (65,536 pages of 32 KiB).
 ``decode_b64_s8192_g8`` B=64, Hq=64, Hkv=8, D=128, page 16, L=8192, 1 GiB per
                     cache (32,768 pages of 32 KiB).
+``prefill_b4_s1024``  causal prefill bf16, B=4, Sq=L=1024, Hq=32, Hkv=8, D=128,
+                    page 16.
+``prefill_b1_s4096``  causal prefill bf16, B=1, Sq=L=4096, Hq=64, Hkv=8, D=128,
+                    page 16.
 """
 
 from __future__ import annotations
@@ -91,6 +95,12 @@ WORKLOADS = {
     "decode_b64_s8192_g8": WorkloadSpec("decode_b64_s8192_g8", "bf16", 64, 1, 64, 8, 128, 16, False,
                                         (0,), 6,
                                         "decode bf16 B=64 Hq=64 Hkv=8 D=128 page16 Skv=8192"),
+    "prefill_b4_s1024": WorkloadSpec("prefill_b4_s1024", "bf16", 4, 1024, 32, 8, 128, 16, True,
+                                     (0,), 7,
+                                     "causal prefill bf16 B=4 Sq=L=1024 Hq=32 Hkv=8 D=128 page16"),
+    "prefill_b1_s4096": WorkloadSpec("prefill_b1_s4096", "bf16", 1, 4096, 64, 8, 128, 16, True,
+                                     (0,), 8,
+                                     "causal prefill bf16 B=1 Sq=L=4096 Hq=64 Hkv=8 D=128 page16"),
 }
 
 WORKLOAD_ORDER = ["tiny_f32", "prefill_f16", "ragged_bf16", "llama3_8b_decode", "qwen3_235b_decode"]
@@ -187,6 +197,11 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         b = batch if batch is not None else spec.batch
         lens = list(seq_lens) if seq_lens is not None else [8192] * b
         width, phys = 512, b * 512
+    elif name in ("prefill_b4_s1024", "prefill_b1_s4096"):
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [spec.seq_q] * b
+        width = -(-spec.seq_q // ps)
+        phys = b * width
     else:
         raise KeyError(name)
 
@@ -237,6 +252,19 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         page_bytes = ps * hkv * d * k_cache.element_size()
         inputs.notes["max_used_page_start_bytes"] = int(used.max()) * page_bytes
     return inputs
+
+
+def attention_flops(inputs: PagedInputs) -> int:
+    """Algorithmic FLOPs of one call: 2 per multiply-add of q.k and of p.v over
+    the keys each query row may see (causal rows see a prefix)."""
+    spec = inputs.spec
+    sq, hq, d = inputs.q.shape[1], inputs.q.shape[2], inputs.q.shape[3]
+    total = 0
+    for seq_len in inputs.seq_lens_host:
+        for i in range(sq):
+            seen = seq_len if not inputs.causal else max(0, min(seq_len, seq_len - sq + i + 1))
+            total += seen
+    return 4 * d * hq * total
 
 
 def kv_bytes(inputs: PagedInputs) -> int:
