@@ -325,3 +325,23 @@ def test_prefill_b4_s1024_full_size_sampled():
 def test_prefill_b1_s4096_full_size_sampled():
     say("prefill_b1_s4096 full size, sampled rows")
     _prefill_full_size("prefill_b1_s4096", rows=(0, 7, 100, 1000, 2047, 2048, 4000))
+
+
+@pytest.mark.parametrize("dtype,d,ps,hq,hkv,seq_q,lens,causal,splits", [
+    ("f16", 128, 32, 8, 2, 40, [300, 40], True, 1),        # chunked: L > Sq, and L = Sq
+    ("bf16", 128, 16, 16, 2, 33, [33, 500, 70], True, 3),  # G = 8, ragged, splits
+    ("bf16", 64, 32, 4, 4, 100, [100, 37, 260], False, 2),  # non-causal, G = 1
+    ("f16", 64, 16, 8, 1, 64, [64, 64], True, 4),           # G = 8, one kv head
+    ("bf16", 128, 16, 4, 1, 80, [50, 100], True, 1),        # Sq > L: early rows see nothing
+    ("bf16", 128, 32, 32, 8, 16, [16, 1000], True, 5),      # 64 rows per kv head exactly
+])
+def test_prefill_kernel_cases(dtype, d, ps, hq, hkv, seq_q, lens, causal, splits):
+    say(f"prefill {dtype} D={d} ps={ps} G={hq // hkv} Sq={seq_q} lens={lens} causal={causal} S={splits}")
+    w = make_custom(dtype, lens, hq, hkv, d, ps, seq_q=seq_q, causal=causal, seed=21, device=DEV)
+    out, lse, ws = run(w, splits, return_workspace=True, causal=causal)
+    xo, xl = oracle_full(w, causal=causal)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    assert_close(out, xo, tdt, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+    if splits > 1:
+        check_partials(w, splits, ws, causal=causal)
