@@ -3,6 +3,7 @@
 from .paged_attention import (  # noqa: F401
     attend,
     attention,
+    check_pages,
     combine,
     gather_logical,
     key_limit,

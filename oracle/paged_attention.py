@@ -28,7 +28,17 @@ What it computes, and where that is defined:
   position ``L - Sq + i`` and sees keys ``j <= L - Sq + i``.  The rocMLIR
   "Fix split-kv attention masking" page (Technical Details, host reference:
   causal valid-split masking) defines validity per query row from that row's
-  effective key length.
+  effective key length, including a prefix offset when one is given, and
+  treats prefix-causal masking as causal.  With a per-sequence prefix offset
+  ``P_b`` (this build's reading of it), row ``i`` sits at key position
+  ``P_b + i`` instead, whatever the causal flag says.
+* Page-id range check (optional): the rocm-libraries "one K/V resource per
+  page" page (Not in this PR; review, LOW findings) notes that page ids are
+  bounded by slot index only, not checked against the cache's page count.
+  ``check_pages`` is that check: a sequence any of whose first
+  ``ceil(L / page_size)`` ids lies outside ``[0, num_pages)`` is not attended
+  (this build's reading: it counts as empty, so its rows give ``(0, -inf)``),
+  and the smallest such batch index is reported.
 * Split-KV: the key pages of a sequence are cut into ``S`` ranges of
   ``ceil(n / S)`` pages each, the last ranges clamped to ``n`` and possibly
   empty (same page, Technical Details: ceil-division of the iterations per
@@ -59,6 +69,7 @@ __all__ = [
     "split_page_ranges",
     "split_partials",
     "combine",
+    "check_pages",
 ]
 
 
@@ -72,16 +83,22 @@ def kv_head_of(q_head: int, group: int) -> int:
     return q_head // group
 
 
-def key_limit(seq_len: int, seq_q: int, row: int, causal: bool) -> int:
+def key_limit(seq_len: int, seq_q: int, row: int, causal: bool, prefix=None) -> int:
     """Number of leading keys query row ``row`` may see.
 
-    Non-causal: all ``seq_len`` keys.  Causal, bottom-right aligned: the row
-    sits at key position ``seq_len - seq_q + row`` and sees keys up to and
-    including it (clamped to ``[0, seq_len]``).
+    Non-causal without a prefix offset: all ``seq_len`` keys.  Otherwise the
+    row sits at key position ``pos`` and sees keys up to and including it,
+    clamped to ``[0, seq_len]``: ``pos = prefix + row`` when a prefix offset is
+    given (prefix-causal), else ``pos = seq_len - seq_q + row`` (causal,
+    bottom-right aligned).
     """
-    if not causal:
+    if prefix is not None:
+        pos = int(prefix) + int(row)
+    elif causal:
+        pos = int(seq_len) - int(seq_q) + int(row)
+    else:
         return int(seq_len)
-    return max(0, min(int(seq_len), int(seq_len) - int(seq_q) + int(row) + 1))
+    return max(0, min(int(seq_len), pos + 1))
 
 
 def gather_logical(cache, table_row, seq_len: int) -> np.ndarray:
@@ -116,12 +133,14 @@ def attend(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float
     return (p @ values) / denom, float(m + np.log(denom))
 
 
-def attention(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = False):
+def attention(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = False,
+              prefix_offset=None):
     """Exact paged attention, unsplit.
 
     ``q [B, Sq, Hq, D]``, ``k_cache [P, page_size, Hkv, D]``,
     ``v_cache [P, page_size, Hkv, Dv]``, ``block_table [B, >=W]`` (int),
-    ``seq_lens [B]``.  Returns ``out [B, Sq, Hq, Dv]`` and ``lse [B, Sq, Hq]``.
+    ``seq_lens [B]``, ``prefix_offset [B]`` or None.  Returns
+    ``out [B, Sq, Hq, Dv]`` and ``lse [B, Sq, Hq]``.
     """
     q = np.asarray(q, dtype=np.float64)
     batch, seq_q, hq, _ = q.shape
@@ -134,8 +153,9 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: 
         seq_len = int(seq_lens[b])
         keys = gather_logical(k_cache, block_table[b], seq_len)
         values = gather_logical(v_cache, block_table[b], seq_len)
+        prefix = None if prefix_offset is None else int(prefix_offset[b])
         for i in range(seq_q):
-            lim = key_limit(seq_len, seq_q, i, causal)
+            lim = key_limit(seq_len, seq_q, i, causal, prefix)
             for h in range(hq):
                 kvh = kv_head_of(h, group)
                 out[b, i, h], lse[b, i, h] = attend(
@@ -157,7 +177,7 @@ def split_page_ranges(n_pages: int, num_splits: int):
 
 
 def split_partials(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool,
-                   num_splits: int):
+                   num_splits: int, prefix_offset=None):
     """Per-split normalised outputs and LSEs.
 
     Returns ``part_out [B, Sq, Hq, S, Dv]`` and ``part_lse [B, Sq, Hq, S]``.
@@ -177,8 +197,9 @@ def split_partials(q, k_cache, v_cache, block_table, seq_lens, scale: float, cau
         keys = gather_logical(k_cache, block_table[b], seq_len)
         values = gather_logical(v_cache, block_table[b], seq_len)
         ranges = split_page_ranges(pages_for(seq_len, page_size), num_splits)
+        prefix = None if prefix_offset is None else int(prefix_offset[b])
         for i in range(seq_q):
-            lim = key_limit(seq_len, seq_q, i, causal)
+            lim = key_limit(seq_len, seq_q, i, causal, prefix)
             for k, (first, end) in enumerate(ranges):
                 lo = first * page_size
                 hi = min(end * page_size, lim)
@@ -218,3 +239,27 @@ def combine(part_out, part_lse):
         out[r] = (w @ flat_o[r]) / total
         lse[r] = m + math.log(total)
     return out.reshape(lead + (dv,)), lse.reshape(lead)
+
+
+def check_pages(block_table, seq_lens, page_size: int, num_pages: int):
+    """Page-id range check over the slots each sequence reads.
+
+    Sequence ``b`` reads slots ``[0, ceil(L_b / page_size))`` of its table row;
+    it passes when every id there lies in ``[0, num_pages)``.  Returns
+    ``(first_bad, lens)``: the smallest failing batch index (-1 when none
+    fails) and the lengths as attended, ``L_b`` for a passing sequence and 0
+    for a failing one.  Slots past a sequence's pages are never looked at.
+    """
+    first_bad = -1
+    lens = []
+    for b in range(len(seq_lens)):
+        seq_len = int(seq_lens[b])
+        ok = True
+        for s in range(pages_for(seq_len, page_size)):
+            page = int(block_table[b][s])
+            if page < 0 or page >= int(num_pages):
+                ok = False
+        if not ok and first_bad < 0:
+            first_bad = b
+        lens.append(seq_len if ok else 0)
+    return first_bad, lens

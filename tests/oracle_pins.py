@@ -116,8 +116,10 @@ def random_problem(rng, batch=3, seq_q=1, hq=4, hkv=2, d=3, dv=None, ps=2, lens=
                 seq_lens=np.array(lens, dtype=np.int64), scale=1.0 / math.sqrt(d))
 
 
-def brute_force(q, k_cache, v_cache, block_table, seq_lens, scale, causal):
-    """Pure-Python attention: one key at a time, straight from the page table."""
+def brute_force(q, k_cache, v_cache, block_table, seq_lens, scale, causal, prefix=None):
+    """Pure-Python attention: one key at a time, straight from the page table.
+    With ``prefix`` (one offset per sequence) row i sits at key prefix[b] + i
+    and the causal mask applies."""
     batch, seq_q, hq, d = q.shape
     ps, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
     group = hq // hkv
@@ -126,12 +128,13 @@ def brute_force(q, k_cache, v_cache, block_table, seq_lens, scale, causal):
     for b in range(batch):
         length = int(seq_lens[b])
         for i in range(seq_q):
-            position = length - seq_q + i
+            masked = causal or prefix is not None
+            position = length - seq_q + i if prefix is None else int(prefix[b]) + i
             for h in range(hq):
                 kvh = h // group
                 scores, rows = [], []
                 for j in range(length):
-                    if causal and j > position:
+                    if masked and j > position:
                         continue
                     page = int(block_table[b][j // ps])
                     slot = j % ps
@@ -168,6 +171,15 @@ def check_brute_force(seed=0):
         bout, blse = brute_force(*args, causal)
         _close(out, bout, 1e-12)
         _close(lse, blse, 1e-12)
+    # prefix-causal: offsets below 0, inside, at and past the sequence
+    p = random_problem(rng, batch=4, seq_q=3, hq=4, hkv=2, d=3, ps=2, lens=[5, 7, 2, 6])
+    args = (p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], p["scale"])
+    for prefix in ([-2, 3, 2, 0], [1, 0, -1, 9], [4, 6, 0, 3]):
+        for causal in (False, True):
+            out, lse = O.attention(*args, causal, prefix_offset=prefix)
+            bout, blse = brute_force(*args, causal, prefix=prefix)
+            _close(out, bout, 1e-12)
+            _close(lse, blse, 1e-12)
 
 
 def check_q_zero_decode(seed=1):
@@ -204,6 +216,79 @@ def check_q_zero_causal(seed=2):
                             for j in range(visible)]
                     _close(out[b, i, h], np.mean(rows, axis=0), 1e-12)
                     _close(lse[b, i, h], math.log(visible), 1e-12)
+
+
+def check_prefix_q_zero():
+    """q = 0 with prefix offsets: lse = ln(keys visible); the counts below are
+    worked out by hand for L = 10, Sq = 4 (row i sits at key prefix + i)."""
+    rng = np.random.default_rng(11)
+    p = random_problem(rng, batch=4, seq_q=4, hq=2, hkv=1, d=2, ps=3, lens=[10, 10, 10, 10])
+    p["q"][:] = 0.0
+    prefix = [4, -2, 12, 0]
+    visible = [[5, 6, 7, 8],      # keys 0..4, 0..5, 0..6, 0..7
+               [0, 0, 1, 2],      # rows at -2 and -1 see nothing
+               [10, 10, 10, 10],  # past the end: every key
+               [1, 2, 3, 4]]
+    for causal in (False, True):
+        out, lse = O.attention(p["q"], p["k_cache"], p["v_cache"], p["block_table"],
+                               p["seq_lens"], p["scale"], causal, prefix_offset=prefix)
+        for b in range(4):
+            for i in range(4):
+                for h in range(2):
+                    n = visible[b][i]
+                    if n == 0:
+                        assert lse[b, i, h] == -math.inf and (out[b, i, h] == 0).all()
+                        continue
+                    rows = [p["v_cache"][p["block_table"][b, j // 3], j % 3, 0] for j in range(n)]
+                    _close(out[b, i, h], np.mean(rows, axis=0), 1e-12)
+                    _close(lse[b, i, h], math.log(n), 1e-12)
+
+
+def check_prefix_bottom_right(seed=12):
+    """A prefix offset of L - Sq is bottom-right causal, bit for bit, split or not."""
+    rng = np.random.default_rng(seed)
+    p = random_problem(rng, batch=4, seq_q=3, hq=4, hkv=2, d=3, ps=2, lens=[1, 4, 9, 16], width=8)
+    args = (p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], p["scale"])
+    prefix = [int(x) - 3 for x in p["seq_lens"]]
+    for x, y in zip(O.attention(*args, True), O.attention(*args, False, prefix_offset=prefix)):
+        assert np.array_equal(x, y)
+    for x, y in zip(O.split_partials(*args, True, 3),
+                    O.split_partials(*args, False, 3, prefix_offset=prefix)):
+        assert np.array_equal(x, y)
+
+
+def check_prefix_split_equivalence(seed=13):
+    """With prefix offsets too, combining the split partials gives the unsplit result."""
+    rng = np.random.default_rng(seed)
+    p = random_problem(rng, batch=4, seq_q=3, hq=4, hkv=2, d=3, ps=2, lens=[3, 8, 11, 16], width=8)
+    args = (p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], p["scale"])
+    prefix = [-1, 2, 20, 7]
+    out, lse = O.attention(*args, False, prefix_offset=prefix)
+    assert np.isinf(lse[0, 0]).all() and np.isfinite(lse[1]).all()
+    for splits in (1, 2, 3, 5, 8):
+        po, pl = O.split_partials(*args, False, splits, prefix_offset=prefix)
+        assert not np.isnan(po).any()
+        co, cl = O.combine(po, pl)
+        _close(co, out, 1e-12)
+        _close(cl, lse, 1e-12)
+
+
+def check_page_range():
+    """Page-id range check on hand-made tables (page size 4, 6 pages)."""
+    table = [[0, 5, UNMAPPED],     # L = 8: slots 0, 1 read, both in range
+             [5, 6, 0],            # L = 5: slot 1 holds 6 = num_pages
+             [3, -1, 2],           # L = 9: slot 1 negative
+             [1, UNMAPPED, -7],    # L = 4: one slot read; the rest never looked at
+             [UNMAPPED, 9, 9],     # L = 0: nothing read
+             [2, 4, 5]]            # L = 12: all three slots, all in range
+    lens = [8, 5, 9, 4, 0, 12]
+    first_bad, attended = O.check_pages(table, lens, 4, 6)
+    assert first_bad == 1
+    assert attended == [8, 0, 0, 4, 0, 12]
+    assert O.check_pages(table[2:], lens[2:], 4, 6) == (0, [0, 4, 0, 12])
+    assert O.check_pages(table[3:], lens[3:], 4, 6) == (-1, [4, 0, 12])
+    # the same tables against 7 pages: id 6 becomes valid
+    assert O.check_pages(table, lens, 4, 7) == (2, [8, 5, 0, 4, 0, 12])
 
 
 def check_sdpa(seed=3):
@@ -325,4 +410,8 @@ ALL_CHECKS = [
     check_v_ones,
     check_empty,
     check_split_ranges,
+    check_prefix_q_zero,
+    check_prefix_bottom_right,
+    check_prefix_split_equivalence,
+    check_page_range,
 ]

@@ -11,6 +11,7 @@ import oracle_pins
 _orig_attend = O.attend
 _orig_key_limit = O.key_limit
 _orig_gather = O.gather_logical
+_orig_check_pages = O.check_pages
 
 
 def attend_no_scale(q_row, keys, values, scale):
@@ -33,16 +34,56 @@ def attend_reversed_values(q_row, keys, values, scale):
     return _orig_attend(q_row, keys, values[::-1], scale)
 
 
-def key_limit_off_by_one(seq_len, seq_q, row, causal):
+def key_limit_off_by_one(seq_len, seq_q, row, causal, prefix=None):
+    if prefix is not None:
+        return _orig_key_limit(seq_len, seq_q, row, causal, prefix)
     if not causal:
         return int(seq_len)
     return max(0, min(int(seq_len), int(seq_len) - int(seq_q) + int(row)))
 
 
-def key_limit_top_left(seq_len, seq_q, row, causal):
+def key_limit_top_left(seq_len, seq_q, row, causal, prefix=None):
+    if prefix is not None:
+        return _orig_key_limit(seq_len, seq_q, row, causal, prefix)
     if not causal:
         return int(seq_len)
     return max(0, min(int(seq_len), int(row) + 1))
+
+
+def key_limit_prefix_off_by_one(seq_len, seq_q, row, causal, prefix=None):
+    if prefix is None:
+        return _orig_key_limit(seq_len, seq_q, row, causal)
+    return max(0, min(int(seq_len), int(prefix) + int(row)))
+
+
+def key_limit_prefix_ignores_row(seq_len, seq_q, row, causal, prefix=None):
+    if prefix is None:
+        return _orig_key_limit(seq_len, seq_q, row, causal)
+    return max(0, min(int(seq_len), int(prefix) + 1))
+
+
+def key_limit_prefix_only_when_causal(seq_len, seq_q, row, causal, prefix=None):
+    return _orig_key_limit(seq_len, seq_q, row, causal, prefix if causal else None)
+
+
+def check_pages_whole_row(block_table, seq_lens, page_size, num_pages):
+    first_bad, lens = -1, []
+    for b, length in enumerate(seq_lens):
+        ok = all(0 <= int(x) < num_pages for x in block_table[b])
+        if not ok and first_bad < 0:
+            first_bad = b
+        lens.append(int(length) if ok else 0)
+    return first_bad, lens
+
+
+def check_pages_inclusive_bound(block_table, seq_lens, page_size, num_pages):
+    return _orig_check_pages(block_table, seq_lens, page_size, num_pages + 1)
+
+
+def check_pages_last_bad(block_table, seq_lens, page_size, num_pages):
+    first_bad, lens = _orig_check_pages(block_table, seq_lens, page_size, num_pages)
+    bad = [b for b, (x, y) in enumerate(zip(lens, seq_lens)) if x != int(y)]
+    return (bad[-1] if bad else -1), lens
 
 
 def gather_reversed_pages(cache, table_row, seq_len):
@@ -75,6 +116,12 @@ MUTATIONS = [
     ("attend", attend_reversed_values),
     ("key_limit", key_limit_off_by_one),
     ("key_limit", key_limit_top_left),
+    ("key_limit", key_limit_prefix_off_by_one),
+    ("key_limit", key_limit_prefix_ignores_row),
+    ("key_limit", key_limit_prefix_only_when_causal),
+    ("check_pages", check_pages_whole_row),
+    ("check_pages", check_pages_inclusive_bound),
+    ("check_pages", check_pages_last_bad),
     ("gather_logical", gather_reversed_pages),
     ("split_page_ranges", split_floor_division),
     ("combine", combine_lse_double_max),
