@@ -36,7 +36,8 @@ What it computes, and where that is defined:
   page" page (Not in this PR; review, LOW findings) notes that page ids are
   bounded by slot index only, not checked against the cache's page count.
   ``check_pages`` is that check: a sequence any of whose first
-  ``ceil(L / page_size)`` ids lies outside ``[0, num_pages)`` is not attended
+  ``ceil(L / page_size)`` ids lies outside ``[0, num_pages)``, or whose length
+  lies outside ``[0, W * page_size]`` (the same bound on slot indices), is not attended
   (this build's reading: it counts as empty, so its rows give ``(0, -inf)``),
   and the smallest such batch index is reported.
 * Split-KV: the key pages of a sequence are cut into ``S`` ranges of
@@ -241,24 +242,29 @@ def combine(part_out, part_lse):
     return out.reshape(lead + (dv,)), lse.reshape(lead)
 
 
-def check_pages(block_table, seq_lens, page_size: int, num_pages: int):
+def check_pages(block_table, seq_lens, page_size: int, num_pages: int, width=None):
     """Page-id range check over the slots each sequence reads.
 
     Sequence ``b`` reads slots ``[0, ceil(L_b / page_size))`` of its table row;
-    it passes when every id there lies in ``[0, num_pages)``.  Returns
-    ``(first_bad, lens)``: the smallest failing batch index (-1 when none
-    fails) and the lengths as attended, ``L_b`` for a passing sequence and 0
-    for a failing one.  Slots past a sequence's pages are never looked at.
+    it passes when its length lies in ``[0, width * page_size]`` (``width`` =
+    the table width, the row's length when None) and every id in those slots
+    lies in ``[0, num_pages)``.  Returns ``(first_bad, lens)``: the smallest
+    failing batch index (-1 when none fails) and the lengths as attended,
+    ``L_b`` for a passing sequence and 0 for a failing one.  Slots past a
+    sequence's pages are never looked at, nor any slot of a sequence whose
+    length is out of range.
     """
     first_bad = -1
     lens = []
     for b in range(len(seq_lens)):
         seq_len = int(seq_lens[b])
-        ok = True
-        for s in range(pages_for(seq_len, page_size)):
-            page = int(block_table[b][s])
-            if page < 0 or page >= int(num_pages):
-                ok = False
+        w = len(block_table[b]) if width is None else int(width)
+        ok = 0 <= seq_len <= w * int(page_size)
+        if ok:
+            for s in range(pages_for(seq_len, page_size)):
+                page = int(block_table[b][s])
+                if page < 0 or page >= int(num_pages):
+                    ok = False
         if not ok and first_bad < 0:
             first_bad = b
         lens.append(seq_len if ok else 0)

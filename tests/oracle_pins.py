@@ -289,6 +289,11 @@ def check_page_range():
     assert O.check_pages(table[3:], lens[3:], 4, 6) == (-1, [4, 0, 12])
     # the same tables against 7 pages: id 6 becomes valid
     assert O.check_pages(table, lens, 4, 7) == (2, [8, 5, 0, 4, 0, 12])
+    # lengths past the table (3 slots of 4 tokens) or negative are rejected unread
+    assert O.check_pages(table, [8, 13, -1, 0, 0, 0], 4, 6) == (1, [8, 0, 0, 0, 0, 0])
+    # a table view narrower than its rows: the view's width bounds the length
+    assert O.check_pages([[0, 1, 2], [3, 4, 5]], [8, 9], 4, 6) == (-1, [8, 9])
+    assert O.check_pages([[0, 1, 2], [3, 4, 5]], [8, 9], 4, 6, width=2) == (1, [8, 0])
 
 
 def check_sdpa(seed=3):

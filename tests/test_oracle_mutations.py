@@ -14,6 +14,12 @@ _orig_gather = O.gather_logical
 _orig_check_pages = O.check_pages
 
 
+def check_pages_length_unbounded(block_table, seq_lens, page_size, num_pages, width=None):
+    lens = [max(0, min(int(x), len(block_table[b]) * page_size)) for b, x in enumerate(seq_lens)]
+    first_bad, att = _orig_check_pages(block_table, lens, page_size, num_pages, width)
+    return first_bad, [a if int(x) == y else y for a, x, y in zip(att, seq_lens, lens)]
+
+
 def attend_no_scale(q_row, keys, values, scale):
     return _orig_attend(q_row, keys, values, 1.0)
 
@@ -66,7 +72,7 @@ def key_limit_prefix_only_when_causal(seq_len, seq_q, row, causal, prefix=None):
     return _orig_key_limit(seq_len, seq_q, row, causal, prefix if causal else None)
 
 
-def check_pages_whole_row(block_table, seq_lens, page_size, num_pages):
+def check_pages_whole_row(block_table, seq_lens, page_size, num_pages, width=None):
     first_bad, lens = -1, []
     for b, length in enumerate(seq_lens):
         ok = all(0 <= int(x) < num_pages for x in block_table[b])
@@ -76,12 +82,12 @@ def check_pages_whole_row(block_table, seq_lens, page_size, num_pages):
     return first_bad, lens
 
 
-def check_pages_inclusive_bound(block_table, seq_lens, page_size, num_pages):
-    return _orig_check_pages(block_table, seq_lens, page_size, num_pages + 1)
+def check_pages_inclusive_bound(block_table, seq_lens, page_size, num_pages, width=None):
+    return _orig_check_pages(block_table, seq_lens, page_size, num_pages + 1, width)
 
 
-def check_pages_last_bad(block_table, seq_lens, page_size, num_pages):
-    first_bad, lens = _orig_check_pages(block_table, seq_lens, page_size, num_pages)
+def check_pages_last_bad(block_table, seq_lens, page_size, num_pages, width=None):
+    first_bad, lens = _orig_check_pages(block_table, seq_lens, page_size, num_pages, width)
     bad = [b for b, (x, y) in enumerate(zip(lens, seq_lens)) if x != int(y)]
     return (bad[-1] if bad else -1), lens
 
@@ -122,6 +128,7 @@ MUTATIONS = [
     ("check_pages", check_pages_whole_row),
     ("check_pages", check_pages_inclusive_bound),
     ("check_pages", check_pages_last_bad),
+    ("check_pages", check_pages_length_unbounded),
     ("gather_logical", gather_reversed_pages),
     ("split_page_ranges", split_floor_division),
     ("combine", combine_lse_double_max),
