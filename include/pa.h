@@ -28,7 +28,8 @@
  *  - Every argument check runs on the host before anything is launched.  A
  *    failed check returns a negative pa_status and writes nothing.  A launch
  *    failure returns PA_EHIP.  No C++ exception crosses this interface.
- *  - q, k_cache and v_cache must be 16-byte aligned (else PA_EINVAL).
+ *  - q, k_cache and v_cache must be 16-byte aligned, block_table and
+ *    seq_lens 4-byte aligned (else PA_EINVAL).
  *  - Tensors are dense and row-major unless a stride is given:
  *      q            [B, Sq, Hq, D]                 dtype
  *      k_cache      [num_pages, page_size, Hkv, D]  dtype
@@ -141,6 +142,60 @@ int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const 
                const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
                int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * Optional inputs of pa_decode_ex and pa_prefill_ex.  A NULL pointer to this
+ * struct, or one whose pointers are all NULL, gives exactly pa_decode /
+ * pa_prefill.  Both arrays are device memory owned by the caller, 4-byte
+ * aligned (else PA_EINVAL); page_check must not overlap any other argument.
+ *
+ *  prefix_offset  [B] int32 or NULL.  When given, row i of sequence b sits at
+ *                 key position prefix_offset[b] + i and sees the keys
+ *                 j <= prefix_offset[b] + i with j < seq_lens[b]
+ *                 (prefix-causal masking, which is causal whatever `causal`
+ *                 says).  Any int32 value is allowed: a row placed before key
+ *                 0 sees nothing (out = 0, lse = -inf), a row at or past the
+ *                 last key sees every key.  prefix_offset[b] = seq_lens[b] - Sq
+ *                 is bottom-right causal masking.  Source: rocMLIR "Fix
+ *                 split-kv attention masking and sweep RMS", Technical
+ *                 Details (host reference: each row's effective key length
+ *                 includes the prefix offset; prefix-causal counts as causal).
+ *  page_check     [B + 1] int32 or NULL.  When given, a check pass (two small
+ *                 kernels on `stream`) runs before the attention: sequence b
+ *                 passes when 0 <= seq_lens[b] <= W * page_size and every id
+ *                 in its slots [0, ceil(seq_lens[b] / page_size)) lies in
+ *                 [0, num_pages).  A failing sequence is attended as empty
+ *                 (its rows give out = 0 and lse = -inf, its splits 0 and
+ *                 -inf) and none of its ids is ever dereferenced.  Afterwards
+ *                 page_check[1 + b] holds the length attended (seq_lens[b],
+ *                 or 0 for a failing sequence) and page_check[0] the smallest
+ *                 failing b, or -1 when every sequence passes.  The device-side
+ *                 preconditions above then reduce to readable seq_lens and
+ *                 block-table slots [0, W) of each row.  Source: rocm-libraries
+ *                 "one K/V resource per page on the gfx942 2D i64 path", Not
+ *                 in this PR (page ids are bounded by slot index but not
+ *                 checked against the cache's block count, which needs that
+ *                 count as a kernel argument) and the review's LOW findings.
+ */
+typedef struct pa_options {
+  const int32_t* prefix_offset;
+  int32_t* page_check;
+} pa_options;
+
+/* pa_decode with the optional inputs above; same arguments and results. */
+int pa_decode_ex(const pa_shape* shape, const pa_options* options, const void* q,
+                 const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_prefill with the optional inputs above; same arguments and results.  With
+ * prefix_offset, sequences may hold fewer than Sq real query rows (chunked or
+ * variable-length prefill padded to Sq): rows past a sequence's own queries
+ * are computed like the others and may be ignored by the caller. */
+int pa_prefill_ex(const pa_shape* shape, const pa_options* options, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_combine -- log-sum-exp merge of split-KV partials, in float32 for every

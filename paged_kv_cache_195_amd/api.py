@@ -22,8 +22,8 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, -1, -2, -3, -4
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 # The functions include/pa.h declares.
-EXPORTS = ("pa_decode", "pa_prefill", "pa_combine", "pa_workspace_bytes",
-           "pa_resolve_num_splits", "pa_strerror")
+EXPORTS = ("pa_decode", "pa_prefill", "pa_decode_ex", "pa_prefill_ex", "pa_combine",
+           "pa_workspace_bytes", "pa_resolve_num_splits", "pa_strerror")
 
 
 class PaShape(ctypes.Structure):
@@ -41,6 +41,15 @@ class PaShape(ctypes.Structure):
         ("num_pages", ctypes.c_int64),
         ("max_pages_per_seq", ctypes.c_int32),
         ("block_table_stride", ctypes.c_int64),
+    ]
+
+
+class PaOptions(ctypes.Structure):
+    """Mirror of ``pa_options``."""
+
+    _fields_ = [
+        ("prefix_offset", ctypes.c_void_p),
+        ("page_check", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_prefill.argtypes = attn_args
     lib.pa_prefill.restype = ctypes.c_int
+    ex_args = attn_args[:1] + [ctypes.POINTER(PaOptions)] + attn_args[1:]
+    lib.pa_decode_ex.argtypes = ex_args
+    lib.pa_decode_ex.restype = ctypes.c_int
+    lib.pa_prefill_ex.argtypes = ex_args
+    lib.pa_prefill_ex.restype = ctypes.c_int
     lib.pa_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.pa_combine.restype = ctypes.c_int
     lib.pa_workspace_bytes.argtypes = [shape_p, ctypes.c_int]
@@ -123,13 +137,23 @@ def _validate_tensors(q, k_cache, v_cache, block_table, seq_lens):
         raise ValueError("block_table and seq_lens need one row per sequence")
 
 
+def _int32_vector(name, t, n):
+    if t is None:
+        return
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of >= {n} elements")
+
+
 def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causal, num_splits,
-               out, lse, num_pages, workspace, return_workspace):
+               out, lse, num_pages, workspace, return_workspace, prefix_offset=None,
+               page_check=None):
     lib = load_library()
     _validate_tensors(q, k_cache, v_cache, block_table, seq_lens)
     shape = make_shape(q, k_cache, v_cache, block_table, num_pages)
     batch, seq_q, hq, _ = q.shape
     dv = v_cache.shape[3]
+    _int32_vector("prefix_offset", prefix_offset, batch)
+    _int32_vector("page_check", page_check, batch + 1)
     if out is None:
         out = torch.empty((batch, seq_q, hq, dv), dtype=q.dtype, device=q.device)
     elif not out.is_contiguous() or out.dtype != q.dtype or out.numel() != batch * seq_q * hq * dv:
@@ -143,10 +167,16 @@ def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causa
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    status = getattr(lib, fn_name)(
-        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(seq_lens), ctypes.c_float(scale), int(bool(causal)), int(num_splits), _ptr(out),
-        _ptr(lse), _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+            ctypes.c_float(scale), int(bool(causal)), int(num_splits), _ptr(out), _ptr(lse),
+            _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+    if prefix_offset is None and page_check is None:
+        status = getattr(lib, fn_name)(ctypes.byref(shape), *args)
+    else:
+        fn_name += "_ex"
+        opts = PaOptions(prefix_offset=None if prefix_offset is None else prefix_offset.data_ptr(),
+                         page_check=None if page_check is None else page_check.data_ptr())
+        status = getattr(lib, fn_name)(ctypes.byref(shape), ctypes.byref(opts), *args)
     _check(status, fn_name)
     if return_workspace:
         return out, lse, workspace
@@ -155,13 +185,16 @@ def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causa
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = False,
            num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
-           workspace=None, return_workspace: bool = False):
+           workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None):
     """Paged decode.  ``q`` is ``[B, Hq, D]`` or ``[B, 1, Hq, D]``; returns
-    ``(out, lse)`` shaped like ``q`` (``lse`` without the head-dim axis)."""
+    ``(out, lse)`` shaped like ``q`` (``lse`` without the head-dim axis).
+    ``prefix_offset`` ([B] int32) and ``page_check`` ([B + 1] int32, written)
+    are the optional inputs of ``pa_decode_ex``."""
     squeeze = q.dim() == 3
     q4 = q.unsqueeze(1) if squeeze else q
     res = _attention("pa_decode", q4, k_cache, v_cache, block_table, seq_lens, scale, causal,
-                     num_splits, out, lse, num_pages, workspace, return_workspace)
+                     num_splits, out, lse, num_pages, workspace, return_workspace,
+                     prefix_offset, page_check)
     if squeeze:
         res = (res[0].squeeze(1), res[1].squeeze(1)) + tuple(res[2:])
     return res
@@ -169,10 +202,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: boo
 
 def prefill(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = True,
             num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
-            workspace=None, return_workspace: bool = False):
-    """Paged prefill: ``q [B, Sq, Hq, D]`` are the last Sq positions of each sequence."""
+            workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None):
+    """Paged prefill: ``q [B, Sq, Hq, D]`` are the last Sq positions of each
+    sequence, or, with ``prefix_offset`` ([B] int32), positions
+    ``prefix_offset[b] + i``.  ``page_check`` ([B + 1] int32) turns on the
+    page-id range check and receives its result (``pa_prefill_ex``)."""
     return _attention("pa_prefill", q, k_cache, v_cache, block_table, seq_lens, scale, causal,
-                      num_splits, out, lse, num_pages, workspace, return_workspace)
+                      num_splits, out, lse, num_pages, workspace, return_workspace,
+                      prefix_offset, page_check)
 
 
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,

@@ -31,6 +31,7 @@ SOURCES = [
     "attn_mfma_f16.hip",
     "attn_mfma_bf16.hip",
     "combine.hip",
+    "page_check.hip",
 ]
 
 COMMON_FLAGS = [

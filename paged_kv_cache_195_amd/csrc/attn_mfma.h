@@ -136,16 +136,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
 
   const int seq_len = p.seq_lens[b];
   const int n_pages = (seq_len + PS - 1) / PS;
+  const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
 
   // ---- this lane's row (row li of the 16) and the key limits of the group
   auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
-    const int i = r_lin / G;
-    int l = seq_len;
-    if (p.causal) {
-      l = seq_len - Sq + i + 1;
-      l = l < 0 ? 0 : (l > seq_len ? seq_len : l);
-    }
-    return l;
+    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
   };
   const int my_r = rg * 16 + li;
   const bool my_valid = my_r < p.rows_per_kvh;

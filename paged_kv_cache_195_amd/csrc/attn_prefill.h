@@ -71,15 +71,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
 
   const int seq_len = p.seq_lens[b];
   const int n_pages = (seq_len + PS - 1) / PS;
+  const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
 
   auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
-    const int i = r_lin / G;
-    int l = seq_len;
-    if (p.causal) {
-      l = seq_len - Sq + i + 1;
-      l = l < 0 ? 0 : (l > seq_len ? seq_len : l);
-    }
-    return l;
+    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
   };
   // rows of the workgroup: [wg_first, +16 RB NW); the last one sees the most keys
   const int wg_first = rg * kRowsPerWaveQ * NW;

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(NW * 64) void attn_valu_kernel(const AttnParams p) 
 
   const int seq_len = p.seq_lens[b];
   const int n_pages = (seq_len + PS - 1) / PS;
+  const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
 
-  // ---- rows of this wave's kv head: query, key limit (causal: bottom-right)
+  // ---- rows of this wave's kv head: query, key limit (causal: bottom-right
+  // or from the prefix offset)
   u32x4 qv[MR];
   int lim[MR];
   int row_id[MR];  // flat (b, i, h) row index, -1 when past the last row
@@ -88,11 +90,7 @@ __global__ __launch_bounds__(NW * 64) void attn_valu_kernel(const AttnParams p) 
     if (r_lin < p.rows_per_kvh) {
       const int i = r_lin / G;
       const int h = kvh * G + (r_lin - i * G);
-      int l = seq_len;
-      if (p.causal) {
-        l = seq_len - Sq + i + 1;
-        l = l < 0 ? 0 : (l > seq_len ? seq_len : l);
-      }
+      const int l = p.causal ? causal_key_limit(seq_len, pos0, i) : seq_len;
       lim[r] = l;
       row_id[r] = (b * Sq + i) * Hq + h;
       const T* qp = static_cast<const T*>(p.q) + static_cast<int64_t>(row_id[r]) * D + ch * kEpc;

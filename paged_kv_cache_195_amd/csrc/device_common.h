@@ -177,4 +177,20 @@ __device__ __forceinline__ float strided_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Keys [0, limit) that query row i of a sequence may see under causal
+// masking.  pos0 is the key position of row 0: seq_len - Sq (bottom-right
+// alignment) or the sequence's prefix offset.  64-bit arithmetic, so any int32
+// offset is safe; the limit is clamped to [0, seq_len].
+__device__ __forceinline__ int causal_key_limit(int seq_len, int64_t pos0, int i) {
+  const int64_t l = pos0 + i + 1;
+  return l < 0 ? 0 : (l > seq_len ? seq_len : static_cast<int>(l));
+}
+
+// Key position of row 0 of sequence b (see causal_key_limit).
+__device__ __forceinline__ int64_t causal_row0(const int32_t* prefix_offset, int b, int seq_len,
+                                               int seq_q) {
+  return prefix_offset != nullptr ? static_cast<int64_t>(prefix_offset[b])
+                                  : static_cast<int64_t>(seq_len) - seq_q;
+}
+
 }  // namespace pa

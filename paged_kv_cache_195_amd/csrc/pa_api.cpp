@@ -25,6 +25,7 @@ constexpr int64_t kMinAutoPagesPerSplit = 4;
 constexpr size_t kAlign = 256;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool aligned4(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -124,10 +125,10 @@ int check_splits(int num_splits) {
   return (num_splits < 0 || num_splits > kMaxSplits) ? PA_EINVAL : PA_OK;
 }
 
-int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_cache,
-                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                  float scale, int causal, int num_splits, void* out, float* lse,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(s, decode);
   if (st != PA_OK) return st;
   st = check_splits(num_splits);
@@ -138,6 +139,11 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
   if (!isfinite(scale)) return PA_EINVAL;
   // q, k_cache and v_cache are read in 16-byte chunks.
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
+  const int32_t* prefix_offset = opt != nullptr ? opt->prefix_offset : nullptr;
+  int32_t* page_check = opt != nullptr ? opt->page_check : nullptr;
+  if (!aligned4(prefix_offset) || !aligned4(page_check) || !aligned4(seq_lens) ||
+      !aligned4(block_table))
+    return PA_EINVAL;
 
   const pa::AttnPlan plan = plan_for(s, num_splits);
   const size_t need = workspace_for(s, plan.num_splits);
@@ -149,7 +155,8 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
   p.k = k_cache;
   p.v = v_cache;
   p.block_table = block_table;
-  p.seq_lens = seq_lens;
+  p.seq_lens = page_check != nullptr ? page_check + 1 : seq_lens;
+  p.prefix_offset = prefix_offset;
   p.out = out;
   p.lse = lse;
   p.part_out = nullptr;
@@ -168,12 +175,17 @@ int run_attention(const pa_shape* s, bool decode, const void* q, const void* k_c
   p.group = group;
   p.rows_per_kvh = s->seq_q * group;
   p.num_splits = plan.num_splits;
-  p.causal = causal ? 1 : 0;
+  p.causal = (causal != 0 || prefix_offset != nullptr) ? 1 : 0;
   p.heads_per_wg = plan.heads_per_wg;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t err;
+  if (page_check != nullptr) {
+    err = pa::launch_page_check(block_table, s->block_table_stride, seq_lens, s->batch,
+                                s->max_pages_per_seq, s->page_size, s->num_pages, page_check, hs);
+    if (err != hipSuccess) return PA_EHIP;
+  }
   if (plan.mfma) {
     err = s->dtype == PA_F16
               ? pa::launch_attn_mfma_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs)
@@ -209,16 +221,32 @@ int pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const v
               const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
               int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
               void* stream) {
-  return run_attention(shape, true, q, k_cache, v_cache, block_table, seq_lens, scale, causal,
-                       num_splits, out, lse, workspace, workspace_bytes, stream);
+  return run_attention(shape, nullptr, true, q, k_cache, v_cache, block_table, seq_lens, scale,
+                       causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
 int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
                int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
                void* stream) {
-  return run_attention(shape, false, q, k_cache, v_cache, block_table, seq_lens, scale, causal,
-                       num_splits, out, lse, workspace, workspace_bytes, stream);
+  return run_attention(shape, nullptr, false, q, k_cache, v_cache, block_table, seq_lens, scale,
+                       causal, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_ex(const pa_shape* shape, const pa_options* options, const void* q,
+                 const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(shape, options, true, q, k_cache, v_cache, block_table, seq_lens, scale,
+                       causal, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int pa_prefill_ex(const pa_shape* shape, const pa_options* options, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(shape, options, false, q, k_cache, v_cache, block_table, seq_lens, scale,
+                       causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
 int pa_combine(int32_t dtype, int32_t rows, int32_t num_splits, int32_t head_dim_v,

@@ -14,6 +14,7 @@ struct AttnParams {
   const void* v;               // [num_pages, page_size, Hkv, Dv]
   const int32_t* block_table;  // row b at block_table + b * bt_stride
   const int32_t* seq_lens;     // [B]
+  const int32_t* prefix_offset;  // [B] key position of each sequence's row 0, or nullptr
   void* out;                   // [B, Sq, Hq, Dv]           (num_splits == 1)
   float* lse;                  // [B, Sq, Hq] or nullptr     (num_splits == 1)
   float* part_out;             // [B*Sq*Hq, S, Dv]           (num_splits > 1)
@@ -25,7 +26,7 @@ struct AttnParams {
   int32_t group;               // Hq / Hkv
   int32_t rows_per_kvh;        // Sq * group: query rows that share one kv head
   int32_t num_splits;          // S >= 1
-  int32_t causal;
+  int32_t causal;              // 1 also when prefix_offset is set (prefix-causal is causal)
   int32_t heads_per_wg;        // kv heads one workgroup serves (divides Hkv and its wave count)
   float scale_log2;            // scale * log2(e): scores are kept in base 2
 };
@@ -82,6 +83,14 @@ hipError_t launch_attn_mfma_f16(const AttnParams& p, const AttnPlan& plan, int h
                                 int page_size, int batch, hipStream_t stream);
 hipError_t launch_attn_mfma_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
                                  int page_size, int batch, hipStream_t stream);
+
+// Page-id range check: writes result[1 + b] = seq_lens[b] when sequence b's
+// length lies in [0, width * page_size] and its first ceil(len / page_size)
+// ids lie in [0, num_pages), else 0; then result[0] = the smallest failing b,
+// or -1.  Two launches on `stream`.
+hipError_t launch_page_check(const int32_t* block_table, int64_t bt_stride,
+                             const int32_t* seq_lens, int batch, int width, int page_size,
+                             int64_t num_pages, int32_t* result, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,
