@@ -4,6 +4,8 @@ from .paged_attention import (  # noqa: F401
     attend,
     attention,
     check_pages,
+    code_value,
+    dequantize_cache,
     combine,
     gather_logical,
     key_limit,

@@ -50,6 +50,17 @@ What it computes, and where that is defined:
   ``exp(lse_s - max lse)`` (same page, host reference: f32 combine for narrow
   floats; here in f64).
 
+* Quantized pages (optional): K and V may be stored as 8-bit codes, each
+  (page, kv head) slice with one float32 scale, the element being
+  ``scale[page, kv_head] * value(code)``.  The pages name int8 paged attention
+  (rocMLIR "Paged Attention: rocmlir-gen changes", the file list's int8 e2e
+  test) and i8 split-KV attention (split-kv masking page, Motivation), and fp8
+  K/V loaders (per-page resource page, review MEDIUM findings); the scale
+  granularity and the fp8 variant (OCP E4M3: 4 exponent bits with bias 7, 3
+  mantissa bits, subnormals, no infinities, S.1111.111 is NaN) are this
+  build's reading.  ``code_value`` decodes one code from those definitions and
+  ``dequantize_cache`` forms the exact float64 cache the attention then reads.
+
 Every function works in float64 on NumPy arrays; inputs are widened exactly.
 There is no blocking, fusion or reordering beyond the definitions above.
 """
@@ -71,6 +82,8 @@ __all__ = [
     "split_partials",
     "combine",
     "check_pages",
+    "code_value",
+    "dequantize_cache",
 ]
 
 
@@ -269,3 +282,41 @@ def check_pages(block_table, seq_lens, page_size: int, num_pages: int, width=Non
             first_bad = b
         lens.append(seq_len if ok else 0)
     return first_bad, lens
+
+
+def code_value(code: int, kind: str) -> float:
+    """Real value of one 8-bit code.
+
+    ``kind == "int8"``: the two's-complement integer of the byte.
+    ``kind == "fp8_e4m3"``: sign bit, then a 4-bit exponent field ``e`` with
+    bias 7, then a 3-bit mantissa field ``m``.  ``e == 0`` is subnormal,
+    ``m / 8 * 2**-6``; otherwise ``(1 + m / 8) * 2**(e - 7)``; ``e == 15`` with
+    ``m == 7`` is NaN (there is no infinity).
+    """
+    code = int(code) & 0xFF
+    if kind == "int8":
+        return float(code - 256 if code >= 128 else code)
+    if kind != "fp8_e4m3":
+        raise ValueError(kind)
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def dequantize_cache(codes, scales, kind: str) -> np.ndarray:
+    """Exact float64 cache of quantized pages.
+
+    ``codes [P, page_size, H, D]`` (8-bit patterns, any integer dtype) and
+    ``scales [P, H]``: element ``[p, t, h, d]`` is
+    ``scales[p, h] * code_value(codes[p, t, h, d])``.
+    """
+    codes = np.asarray(codes).astype(np.int64) & 0xFF
+    table = np.array([code_value(c, kind) for c in range(256)], dtype=np.float64)
+    values = table[codes]
+    scales = np.asarray(scales, dtype=np.float64)
+    return values * scales[:, None, :, None]

@@ -87,6 +87,44 @@ FIXTURES = {
         "expected_out": [[[[1.0, 0.0]], [[0.5, 0.5]], [[1.0, 1.0]], [[1.75, 0.75]]]],
         "expected_lse": [[[0.0], [math.log(2.0)], [math.log(3.0)], [math.log(4.0)]]],
     },
+    "quantized_hand_case": {
+        "description": "The hand case above with K and V stored as 8-bit codes and one scale per "
+                       "(page, kv head), once as int8 and once as fp8 E4M3. Scales differ between "
+                       "K and V and between pages (one is 0, one negative) so that a scale taken "
+                       "from the wrong cache, page or slot changes the answer.",
+        "citation": "int8 paged attention (rocMLIR 'Paged Attention: rocmlir-gen changes', file "
+                    "list: the int8 e2e test) and i8 split-KV attention (rocMLIR 'Fix split-kv "
+                    "attention masking and sweep RMS', Motivation); fp8 K/V loaders (rocm-libraries "
+                    "'one K/V resource per page on the gfx942 2D i64 path', review). Scale "
+                    "granularity and the fp8 format are this build's reading.",
+        "derivation": "Physical page 0 holds token 1, page 1 holds token 0. int8: k1 = ln3 * (1, 0), "
+                      "k0 = 0 * (5, -3) = (0, 0), v1 = 0.25 * (0, 4) = (0, 1), v0 = -0.5 * (-2, 0) = "
+                      "(1, 0). fp8 (0x38 = 1, 0x50 = 8, 0xC4 = -3, 0x80 = -0, 0x48 = 4, 0xB0 = -0.5): "
+                      "k1 = ln3 * (1, 0), k0 = 0 * (8, -3), v1 = 0.25 * (-0, 4) = (-0, 1), "
+                      "v0 = -2 * (-0.5, 0) = (1, 0). Both give the hand case: out (0.25, 0.75), "
+                      "lse ln 4.",
+        "page_size": 1, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": False,
+        "q": [[[[1.0, 0.0]]]],
+        "block_table": [[1, 0]],
+        "seq_lens": [2],
+        "variants": {
+            "int8": {
+                "k_codes": [[[[1, 0]]], [[[5, 0xFD]]]],
+                "v_codes": [[[[0, 4]]], [[[0xFE, 0]]]],
+                "k_scales": [[math.log(3.0)], [0.0]],
+                "v_scales": [[0.25], [-0.5]],
+            },
+            "fp8_e4m3": {
+                "k_codes": [[[[0x38, 0x00]]], [[[0x50, 0xC4]]]],
+                "v_codes": [[[[0x80, 0x48]]], [[[0xB0, 0x00]]]],
+                "k_scales": [[math.log(3.0)], [0.0]],
+                "v_scales": [[0.25], [-2.0]],
+            },
+        },
+        "expected_out": [[[[0.25, 0.75]]]],
+        "expected_lse": [[[math.log(4.0)]]],
+    },
 }
 
 

@@ -296,6 +296,97 @@ def check_page_range():
     assert O.check_pages([[0, 1, 2], [3, 4, 5]], [8, 9], 4, 6, width=2) == (1, [8, 0])
 
 
+def check_code_values():
+    """8-bit codes: special fp8 values worked out by hand from the format, and
+    every code against torch's float8_e4m3fn and NumPy's int8 decoding."""
+    import torch
+
+    hand = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x48: 4.0, 0x50: 8.0, 0x7E: 448.0,
+            0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0xB0: -0.5, 0xB8: -1.0,
+            0xC4: -3.0, 0xFE: -448.0}
+    for code, value in hand.items():
+        assert O.code_value(code, "fp8_e4m3") == value, hex(code)
+    assert math.isnan(O.code_value(0x7F, "fp8_e4m3")) and math.isnan(O.code_value(0xFF, "fp8_e4m3"))
+    assert math.copysign(1.0, O.code_value(0x80, "fp8_e4m3")) == -1.0
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mine = np.array([O.code_value(c, "fp8_e4m3") for c in range(256)])
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(mine)) and np.array_equal(lib[~nan], mine[~nan])
+    ints = np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64)
+    assert [O.code_value(c, "int8") for c in range(256)] == ints.tolist()
+
+
+def check_golden_quantized():
+    """The hand case stored as int8 and as fp8 codes with per-(page, kv head) scales."""
+    with open(os.path.join(GOLDEN, "quantized_hand_case.json")) as f:
+        g = json.load(f)
+    for kind, v in g["variants"].items():
+        k = O.dequantize_cache(np.array(v["k_codes"]), np.array(v["k_scales"]), kind)
+        vv = O.dequantize_cache(np.array(v["v_codes"]), np.array(v["v_scales"]), kind)
+        out, lse = O.attention(np.array(g["q"]), k, vv, np.array(g["block_table"]),
+                               np.array(g["seq_lens"]), g["scale"], g["causal"])
+        _close(out, np.array(g["expected_out"]), 1e-15)
+        _close(lse, np.array(g["expected_lse"]), 1e-15)
+
+
+def check_quantized_scale_placement():
+    """q = 0, so every output is the mean of the visible V rows; the means below
+    are worked out by hand.  Hkv = 2 (G = 2), page size 2, L = 3, table [1, 0]:
+    tokens 0 and 1 live in page 1, token 2 in page 0; V codes are 1 in kv head
+    0 and 2 in kv head 1; V scales [page][kv head] = [[6, 1], [3, 7], [100, 100]].
+    kv head 0: (3 + 3 + 6) / 3 = 4; kv head 1: (14 + 14 + 2) / 3 = 10."""
+    for kind, one, two in (("int8", 1, 2), ("fp8_e4m3", 0x38, 0x40)):
+        v_codes = np.zeros((3, 2, 2, 4), dtype=np.int64)
+        v_codes[:, :, 0, :] = one
+        v_codes[:, :, 1, :] = two
+        v_scales = np.array([[6.0, 1.0], [3.0, 7.0], [100.0, 100.0]])
+        k_codes = np.zeros((3, 2, 2, 4), dtype=np.int64)
+        k_scales = np.ones((3, 2))
+        q = np.zeros((1, 1, 4, 4))
+        table = np.array([[1, 0, UNMAPPED]])
+        out, lse = O.attention(q, O.dequantize_cache(k_codes, k_scales, kind),
+                               O.dequantize_cache(v_codes, v_scales, kind), table,
+                               np.array([3]), 0.5, False)
+        _close(out[0, 0, :2], np.full((2, 4), 4.0), 1e-13)
+        _close(out[0, 0, 2:], np.full((2, 4), 10.0), 1e-13)
+        _close(lse, np.full((1, 1, 4), math.log(3.0)), 1e-13)
+
+
+def quantized_problem(rng, kind, batch=3, seq_q=2, hq=4, hkv=2, d=4, ps=2, lens=(3, 7, 10)):
+    """Random codes (fp8 NaN codes excluded) and scales of both signs."""
+    p = random_problem(rng, batch=batch, seq_q=seq_q, hq=hq, hkv=hkv, d=d, ps=ps, lens=list(lens),
+                       poison=False)
+    phys = p["k_cache"].shape[0]
+    allowed = np.array([c for c in range(256) if kind == "int8" or (c & 0x7F) != 0x7F])
+    p["k_codes"] = rng.choice(allowed, size=(phys, ps, hkv, d))
+    p["v_codes"] = rng.choice(allowed, size=(phys, ps, hkv, d))
+    p["k_scales"] = rng.uniform(-1.0, 1.0, size=(phys, hkv)) / (40.0 if kind == "int8" else 1.0)
+    p["v_scales"] = rng.uniform(-1.0, 1.0, size=(phys, hkv))
+    return p
+
+
+def check_quantized_scale_laws(seed=14):
+    """Multiplying every V scale by c multiplies the output by c and leaves the
+    LSE alone; multiplying every K scale by c equals multiplying the softmax
+    scale by c."""
+    rng = np.random.default_rng(seed)
+    for kind in ("int8", "fp8_e4m3"):
+        p = quantized_problem(rng, kind)
+        k = O.dequantize_cache(p["k_codes"], p["k_scales"], kind)
+        v = O.dequantize_cache(p["v_codes"], p["v_scales"], kind)
+        rest = (p["block_table"], p["seq_lens"])
+        out, lse = O.attention(p["q"], k, v, *rest, p["scale"], True)
+        v4 = O.dequantize_cache(p["v_codes"], p["v_scales"] * 4.0, kind)
+        out4, lse4 = O.attention(p["q"], k, v4, *rest, p["scale"], True)
+        _close(out4, 4.0 * out, 1e-12)
+        _close(lse4, lse, 1e-12)
+        k3 = O.dequantize_cache(p["k_codes"], p["k_scales"] * 3.0, kind)
+        out3, lse3 = O.attention(p["q"], k3, v, *rest, p["scale"], True)
+        outs, lses = O.attention(p["q"], k, v, *rest, p["scale"] * 3.0, True)
+        _close(out3, outs, 1e-12)
+        _close(lse3, lses, 1e-12)
+
+
 def check_sdpa(seed=3):
     """Unpaged special case against torch's float64 scaled_dot_product_attention."""
     import torch
@@ -419,4 +510,8 @@ ALL_CHECKS = [
     check_prefix_bottom_right,
     check_prefix_split_equivalence,
     check_page_range,
+    check_code_values,
+    check_golden_quantized,
+    check_quantized_scale_placement,
+    check_quantized_scale_laws,
 ]

@@ -12,6 +12,35 @@ _orig_attend = O.attend
 _orig_key_limit = O.key_limit
 _orig_gather = O.gather_logical
 _orig_check_pages = O.check_pages
+_orig_code_value = O.code_value
+_orig_dequantize = O.dequantize_cache
+
+
+def code_value_fp8_bias8(code, kind):
+    v = _orig_code_value(code, kind)
+    return v / 2.0 if kind == "fp8_e4m3" else v
+
+
+def code_value_fp8_subnormal(code, kind):
+    if kind == "fp8_e4m3" and (int(code) >> 3) & 0xF == 0:
+        return _orig_code_value(code, kind) / 2.0
+    return _orig_code_value(code, kind)
+
+
+def code_value_int8_unsigned(code, kind):
+    return float(int(code) & 0xFF) if kind == "int8" else _orig_code_value(code, kind)
+
+
+def dequantize_no_scale(codes, scales, kind):
+    return _orig_dequantize(codes, np.ones_like(np.asarray(scales, dtype=np.float64)), kind)
+
+
+def dequantize_heads_reversed(codes, scales, kind):
+    return _orig_dequantize(codes, np.asarray(scales)[:, ::-1], kind)
+
+
+def dequantize_pages_reversed(codes, scales, kind):
+    return _orig_dequantize(codes, np.asarray(scales)[::-1], kind)
 
 
 def check_pages_length_unbounded(block_table, seq_lens, page_size, num_pages, width=None):
@@ -129,6 +158,12 @@ MUTATIONS = [
     ("check_pages", check_pages_inclusive_bound),
     ("check_pages", check_pages_last_bad),
     ("check_pages", check_pages_length_unbounded),
+    ("code_value", code_value_fp8_bias8),
+    ("code_value", code_value_fp8_subnormal),
+    ("code_value", code_value_int8_unsigned),
+    ("dequantize_cache", dequantize_no_scale),
+    ("dequantize_cache", dequantize_heads_reversed),
+    ("dequantize_cache", dequantize_pages_reversed),
     ("gather_logical", gather_reversed_pages),
     ("split_page_ranges", split_floor_division),
     ("combine", combine_lse_double_max),
