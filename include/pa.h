@@ -32,8 +32,8 @@
  *    seq_lens 4-byte aligned (else PA_EINVAL).
  *  - Tensors are dense and row-major unless a stride is given:
  *      q            [B, Sq, Hq, D]                 dtype
- *      k_cache      [num_pages, page_size, Hkv, D]  dtype
- *      v_cache      [num_pages, page_size, Hkv, Dv] dtype
+ *      k_cache      [num_pages, page_size, Hkv, D]  dtype (or kv_dtype codes)
+ *      v_cache      [num_pages, page_size, Hkv, Dv] dtype (or kv_dtype codes)
  *      block_table  [B, W] int32, row stride block_table_stride (>= W)
  *      seq_lens     [B] int32
  *      out          [B, Sq, Hq, Dv]                dtype
@@ -61,8 +61,16 @@
 extern "C" {
 #endif
 
-/* Element type of q, k_cache, v_cache and out. */
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element type of q, k_cache, v_cache and out.  PA_I8 and PA_FP8_E4M3 name
+ * 8-bit cache codes and are valid only as pa_shape.kv_dtype. */
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_I8 = 3,       /* two's-complement int8 code                                  */
+  PA_FP8_E4M3 = 4  /* OCP fp8 E4M3: exponent bias 7, subnormals, no infinity,
+                      S.1111.111 is NaN                                          */
+} pa_dtype;
 
 /* Return codes. */
 typedef enum pa_status {
@@ -88,12 +96,17 @@ typedef struct pa_shape {
   int64_t num_pages;          /* physical pages per cache tensor (validation)   */
   int32_t max_pages_per_seq;  /* W: block-table width                           */
   int64_t block_table_stride; /* elements between block-table rows, >= W        */
+  int32_t kv_dtype;           /* 0: k_cache and v_cache hold `dtype`; PA_I8 or
+                                 PA_FP8_E4M3: they hold 8-bit codes, with the
+                                 scales passed in pa_options                    */
 } pa_shape;
 
 /*
  * Supported envelope of this build (else PA_EUNSUPPORTED):
  *   dtype F32, F16 or BF16; D == Dv in {32, 64, 128}; page_size in {16, 32};
  *   any group size Hq / Hkv >= 1; B <= 65535 and Hkv <= 65535.
+ *   8-bit caches (kv_dtype PA_I8 or PA_FP8_E4M3): dtype F16 or BF16 and
+ *   D == Dv in {64, 128}.
  */
 
 /*
@@ -146,8 +159,9 @@ int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const 
 /*
  * Optional inputs of pa_decode_ex and pa_prefill_ex.  A NULL pointer to this
  * struct, or one whose pointers are all NULL, gives exactly pa_decode /
- * pa_prefill.  Both arrays are device memory owned by the caller, 4-byte
- * aligned (else PA_EINVAL); page_check must not overlap any other argument.
+ * pa_prefill (which therefore reject 8-bit caches).  The arrays are device
+ * memory owned by the caller, 4-byte aligned (else PA_EINVAL); page_check
+ * must not overlap any other argument.
  *
  *  prefix_offset  [B] int32 or NULL.  When given, row i of sequence b sits at
  *                 key position prefix_offset[b] + i and sees the keys
@@ -176,10 +190,28 @@ int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const 
  *                 in this PR (page ids are bounded by slot index but not
  *                 checked against the cache's block count, which needs that
  *                 count as a kernel argument) and the review's LOW findings.
+ *  k_scale,       [num_pages, Hkv] float32 each, required exactly when
+ *  v_scale        shape->kv_dtype is PA_I8 or PA_FP8_E4M3 (else PA_EINVAL).
+ *                 Element [p, t, h, d] of the K cache is
+ *                 k_scale[p * Hkv + h] * value(code), value() decoding the
+ *                 code as int8 or as OCP fp8 E4M3; likewise V.  The scales of
+ *                 every page a sequence reads must be finite.  Queries, outputs
+ *                 and arithmetic stay as for 16-bit caches: codes are decoded
+ *                 exactly to the query type and the scales are applied in
+ *                 float32 (to the scores, and to each tile's weighted V sum).
+ *                 Sources: int8 paged attention, rocMLIR "Paged Attention:
+ *                 rocmlir-gen changes" (file list, int8 e2e test); i8 split-KV
+ *                 attention, rocMLIR "Fix split-kv attention masking and sweep
+ *                 RMS" (Motivation); fp8 K/V loaders, rocm-libraries "one K/V
+ *                 resource per page on the gfx942 2D i64 path" (review).  The
+ *                 per-(page, kv head) scale and the OCP variant are this
+ *                 library's choices.
  */
 typedef struct pa_options {
   const int32_t* prefix_offset;
   int32_t* page_check;
+  const float* k_scale;
+  const float* v_scale;
 } pa_options;
 
 /* pa_decode with the optional inputs above; same arguments and results. */

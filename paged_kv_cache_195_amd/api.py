@@ -17,9 +17,11 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_I8, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, -1, -2, -3, -4
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+# 8-bit cache codes (pa_shape.kv_dtype)
+KV_CODE = {torch.int8: PA_I8, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 # The functions include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_prefill", "pa_decode_ex", "pa_prefill_ex", "pa_combine",
@@ -41,6 +43,7 @@ class PaShape(ctypes.Structure):
         ("num_pages", ctypes.c_int64),
         ("max_pages_per_seq", ctypes.c_int32),
         ("block_table_stride", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -50,6 +53,8 @@ class PaOptions(ctypes.Structure):
     _fields_ = [
         ("prefix_offset", ctypes.c_void_p),
         ("page_check", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -118,6 +123,7 @@ def make_shape(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     s.num_pages = k_cache.shape[0] if num_pages is None else int(num_pages)
     s.max_pages_per_seq = block_table.shape[1]
     s.block_table_stride = block_table.stride(0)
+    s.kv_dtype = KV_CODE.get(k_cache.dtype, 0)
     return s
 
 
@@ -127,8 +133,11 @@ def _validate_tensors(q, k_cache, v_cache, block_table, seq_lens):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-        if t.dtype != q.dtype:
-            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a dtype")
+    if k_cache.dtype != q.dtype and k_cache.dtype not in KV_CODE:
+        raise ValueError(f"cache dtype {k_cache.dtype} is neither q's dtype {q.dtype} "
+                         "nor an 8-bit code type (int8, float8_e4m3fn)")
     if block_table.dtype != torch.int32 or not block_table.is_cuda or block_table.stride(1) != 1:
         raise ValueError("block_table must be an int32 GPU tensor with unit column stride")
     if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or not seq_lens.is_contiguous():
@@ -144,9 +153,17 @@ def _int32_vector(name, t, n):
         raise ValueError(f"{name} must be a contiguous int32 GPU tensor of >= {n} elements")
 
 
+def _scales(name, t, k_cache):
+    if t is None:
+        raise ValueError(f"8-bit caches need {name}")
+    if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+            or tuple(t.shape) != (k_cache.shape[0], k_cache.shape[2])):
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor [num_pages, Hkv]")
+
+
 def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causal, num_splits,
                out, lse, num_pages, workspace, return_workspace, prefix_offset=None,
-               page_check=None):
+               page_check=None, k_scale=None, v_scale=None):
     lib = load_library()
     _validate_tensors(q, k_cache, v_cache, block_table, seq_lens)
     shape = make_shape(q, k_cache, v_cache, block_table, num_pages)
@@ -154,6 +171,11 @@ def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causa
     dv = v_cache.shape[3]
     _int32_vector("prefix_offset", prefix_offset, batch)
     _int32_vector("page_check", page_check, batch + 1)
+    if shape.kv_dtype:
+        _scales("k_scale", k_scale, k_cache)
+        _scales("v_scale", v_scale, k_cache)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("scales are for 8-bit caches only")
     if out is None:
         out = torch.empty((batch, seq_q, hq, dv), dtype=q.dtype, device=q.device)
     elif not out.is_contiguous() or out.dtype != q.dtype or out.numel() != batch * seq_q * hq * dv:
@@ -170,12 +192,14 @@ def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causa
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
             ctypes.c_float(scale), int(bool(causal)), int(num_splits), _ptr(out), _ptr(lse),
             _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
-    if prefix_offset is None and page_check is None:
+    if prefix_offset is None and page_check is None and k_scale is None:
         status = getattr(lib, fn_name)(ctypes.byref(shape), *args)
     else:
         fn_name += "_ex"
         opts = PaOptions(prefix_offset=None if prefix_offset is None else prefix_offset.data_ptr(),
-                         page_check=None if page_check is None else page_check.data_ptr())
+                         page_check=None if page_check is None else page_check.data_ptr(),
+                         k_scale=None if k_scale is None else k_scale.data_ptr(),
+                         v_scale=None if v_scale is None else v_scale.data_ptr())
         status = getattr(lib, fn_name)(ctypes.byref(shape), ctypes.byref(opts), *args)
     _check(status, fn_name)
     if return_workspace:
@@ -185,16 +209,18 @@ def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causa
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = False,
            num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
-           workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None):
+           workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None,
+           k_scale=None, v_scale=None):
     """Paged decode.  ``q`` is ``[B, Hq, D]`` or ``[B, 1, Hq, D]``; returns
     ``(out, lse)`` shaped like ``q`` (``lse`` without the head-dim axis).
-    ``prefix_offset`` ([B] int32) and ``page_check`` ([B + 1] int32, written)
-    are the optional inputs of ``pa_decode_ex``."""
+    ``prefix_offset`` ([B] int32), ``page_check`` ([B + 1] int32, written) and,
+    for int8 / float8_e4m3fn caches, ``k_scale`` / ``v_scale`` ([num_pages,
+    Hkv] float32) are the optional inputs of ``pa_decode_ex``."""
     squeeze = q.dim() == 3
     q4 = q.unsqueeze(1) if squeeze else q
     res = _attention("pa_decode", q4, k_cache, v_cache, block_table, seq_lens, scale, causal,
                      num_splits, out, lse, num_pages, workspace, return_workspace,
-                     prefix_offset, page_check)
+                     prefix_offset, page_check, k_scale, v_scale)
     if squeeze:
         res = (res[0].squeeze(1), res[1].squeeze(1)) + tuple(res[2:])
     return res
@@ -202,14 +228,16 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: boo
 
 def prefill(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool = True,
             num_splits: int = 0, out=None, lse=None, num_pages: Optional[int] = None,
-            workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None):
+            workspace=None, return_workspace: bool = False, prefix_offset=None, page_check=None,
+            k_scale=None, v_scale=None):
     """Paged prefill: ``q [B, Sq, Hq, D]`` are the last Sq positions of each
     sequence, or, with ``prefix_offset`` ([B] int32), positions
     ``prefix_offset[b] + i``.  ``page_check`` ([B + 1] int32) turns on the
-    page-id range check and receives its result (``pa_prefill_ex``)."""
+    page-id range check and receives its result; ``k_scale`` / ``v_scale`` go
+    with 8-bit caches (``pa_prefill_ex``)."""
     return _attention("pa_prefill", q, k_cache, v_cache, block_table, seq_lens, scale, causal,
                       num_splits, out, lse, num_pages, workspace, return_workspace,
-                      prefix_offset, page_check)
+                      prefix_offset, page_check, k_scale, v_scale)
 
 
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,

@@ -30,6 +30,8 @@ SOURCES = [
     "attn_valu_bf16.hip",
     "attn_mfma_f16.hip",
     "attn_mfma_bf16.hip",
+    "attn_mfma_q_f16.hip",
+    "attn_mfma_q_bf16.hip",
     "combine.hip",
     "page_check.hip",
 ]

@@ -36,6 +36,15 @@
 // nothing and a zero row sum stores (0, -inf).  V rows of tokens past the
 // sequence length are zeroed in LDS, so NaN in a last page's tail never meets
 // a zero weight in the MFMA.
+//
+// Quantized caches (8-bit codes, one float32 scale per (page, kv head)): each
+// lane loads 16 codes of a row, decodes them to float (int8: one SDWA
+// convert per code; fp8 E4M3: one v_cvt_pk_f32_fp8 per two codes, which
+// decodes the OCP format on gfx950) and packs them to the 16-bit operand
+// type, exactly (a code has at most 8 significant bits, inside the range of
+// both types).  The staged rows then feed the same MFMA steps.  The K scale
+// multiplies the tile's scores; the V scale multiplies the tile's P.V product
+// before it is added to O, so a scale of any sign or size costs no precision.
 #pragma once
 
 #include "device_common.h"
@@ -53,6 +62,36 @@ typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+
+// Element kind of the K/V caches: the operand type itself, or 8-bit codes.
+struct KvSame {};
+struct KvI8 {};
+struct KvFp8 {};
+
+template <typename KV>
+struct KvTraits {
+  static constexpr bool quant = true;
+};
+template <>
+struct KvTraits<KvSame> {
+  static constexpr bool quant = false;
+};
+
+// Four codes of one 32-bit word as floats (exact).
+__device__ __forceinline__ void decode4(KvI8, uint32_t w, float* f) {
+  f[0] = static_cast<float>(static_cast<int8_t>(w & 0xffu));
+  f[1] = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu));
+  f[2] = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu));
+  f[3] = static_cast<float>(static_cast<int8_t>(w >> 24));
+}
+__device__ __forceinline__ void decode4(KvFp8, uint32_t w, float* f) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
 
 template <typename T>
 struct Mfma;
@@ -79,6 +118,12 @@ struct Mfma<bf16_t> {
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_v));
   }
   static constexpr uint32_t kOnes = 0x3f803f80u;  // two packed 1.0
+  // Two floats with at most 8 significant bits as packed bf16: their top
+  // halves (exact).
+  static __device__ __forceinline__ uint32_t pack_exact(float a, float b) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                                 0x07060302u);
+  }
 };
 
 template <>
@@ -100,19 +145,42 @@ struct Mfma<f16_t> {
                                                                  b - static_cast<float>(h[1])));
   }
   static constexpr uint32_t kOnes = 0x3c003c00u;  // two packed 1.0
+  // Two floats that f16 represents exactly (8-bit code values) as packed f16.
+  static __device__ __forceinline__ uint32_t pack_exact(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  }
 };
 
-// T: bf16_t or f16_t; D: head dim (= Dv, a multiple of 32); PS: tokens per
-// page (a multiple of 16); NW: waves per workgroup.  p.heads_per_wg kv heads
-// per workgroup, NW / heads_per_wg waves per head; each workgroup covers 16
-// rows per kv head (row group rg = blockIdx.x / S).
-template <typename T, int D, int PS, int NW>
+// 16 codes (one 16-byte load) as two 16-byte chunks of 8 operand values.
+template <typename T, typename KV>
+__device__ __forceinline__ void widen16(const u32x4& w, u32x4& lo, u32x4& hi) {
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float f[4];
+    decode4(KV{}, word(w, i), f);
+    packed[2 * i] = Mfma<T>::pack_exact(f[0], f[1]);
+    packed[2 * i + 1] = Mfma<T>::pack_exact(f[2], f[3]);
+  }
+  lo = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  hi = u32x4{packed[4], packed[5], packed[6], packed[7]};
+}
+
+// T: bf16_t or f16_t (q, out and the MFMA operands); KV: KvSame (caches of
+// T) or KvI8 / KvFp8 (8-bit codes with p.k_scale / p.v_scale); D: head dim
+// (= Dv, a multiple of 32; >= 64 for codes); PS: tokens per page (a multiple
+// of 16); NW: waves per workgroup.  p.heads_per_wg kv heads per workgroup,
+// NW / heads_per_wg waves per head; each workgroup covers 16 rows per kv head
+// (row group rg = blockIdx.x / S).
+template <typename T, typename KV, int D, int PS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) {
   static_assert(D % 32 == 0 && PS % 16 == 0, "tile shape");
+  constexpr bool kQuant = KvTraits<KV>::quant;
   constexpr int kKSteps = D / 32;         // 16x16x32 steps for q.k
   constexpr int kNBlocks = D / 16;        // 16-dim output blocks
   constexpr int kTiles = PS / 16;         // 16-token tiles per page
-  constexpr int kRowBytes = D * 2;
+  constexpr int kRowBytes = D * 2;        // a staged row (operand type)
+  constexpr int kCacheRowBytes = kQuant ? D : D * 2;  // a row in the cache
   constexpr float kSlack = 8.f;
 
   const int lane = threadIdx.x & 63;
@@ -183,20 +251,21 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
 
   PageTable pt;
   pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kRowBytes;
+  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kCacheRowBytes;
   pt.n_pages = n_pages;
 
   // Whole-row loads: wave load j covers rows j * kRowsPerLoad .. +kRowsPerLoad
   // of the tile; lane l takes 16-byte chunk lc of row lr.
-  constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  constexpr int kRowsPerLoad = 64 / kChunks;   // rows per wave load
-  constexpr int kLoads = 16 / kRowsPerLoad;    // wave loads per tile (= kKSteps)
-  static_assert(kLoads == kKSteps, "one wave load per k-step");
-  const int lr = lane / kChunks;
-  const int lc = lane % kChunks;
-  const uint32_t lane_off = static_cast<uint32_t>((lr * Hkv + kvh) * kRowBytes + 16 * lc);
-  const uint32_t load_step = static_cast<uint32_t>(kRowsPerLoad * Hkv * kRowBytes);
-  const uint32_t tile_step = static_cast<uint32_t>(16 * Hkv * kRowBytes);
+  constexpr int kChunks = D / 8;                      // 16-byte chunks per staged row
+  constexpr int kCacheChunks = kCacheRowBytes / 16;   // 16-byte chunks per cache row
+  constexpr int kRowsPerLoad = 64 / kCacheChunks;     // rows per wave load
+  constexpr int kLoads = 16 / kRowsPerLoad;           // wave loads per tile
+  static_assert(kRowsPerLoad <= 16 && 16 % kRowsPerLoad == 0, "whole rows per tile");
+  const int lr = lane / kCacheChunks;
+  const int lc = lane % kCacheChunks;
+  const uint32_t lane_off = static_cast<uint32_t>((lr * Hkv + kvh) * kCacheRowBytes + 16 * lc);
+  const uint32_t load_step = static_cast<uint32_t>(kRowsPerLoad * Hkv * kCacheRowBytes);
+  const uint32_t tile_step = static_cast<uint32_t>(16 * Hkv * kCacheRowBytes);
   const char* kbase = static_cast<const char*>(p.k);
   const char* vbase = static_cast<const char*>(p.v);
 
@@ -231,16 +300,27 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
           reinterpret_cast<const u32x4*>(vbase + base + off + j * load_step));
   };
 
-  auto consume_tile = [&](int tok0, const u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
+  auto consume_tile = [&](int tok0, const u32x4* kk, u32x4* vv, float ks, float vs)
+                          __attribute__((always_inline)) {
     // stage K and V rows; V rows of tokens past the sequence become zero
     const bool tail = tok0 + 16 > min_lim;  // wave-uniform
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int r = j * kRowsPerLoad + lr;
-      *reinterpret_cast<u32x4*>(lds_k + swz(r, lc)) = kk[j];
       u32x4 vrow = vv[j];
       if (tail && tok0 + r >= seq_len) vrow = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(lds_v + swz(r, lc)) = vrow;
+      if constexpr (kQuant) {
+        u32x4 lo, hi;
+        widen16<T, KV>(kk[j], lo, hi);
+        *reinterpret_cast<u32x4*>(lds_k + swz(r, 2 * lc)) = lo;
+        *reinterpret_cast<u32x4*>(lds_k + swz(r, 2 * lc + 1)) = hi;
+        widen16<T, KV>(vrow, lo, hi);
+        *reinterpret_cast<u32x4*>(lds_v + swz(r, 2 * lc)) = lo;
+        *reinterpret_cast<u32x4*>(lds_v + swz(r, 2 * lc + 1)) = hi;
+      } else {
+        *reinterpret_cast<u32x4*>(lds_k + swz(r, lc)) = kk[j];
+        *reinterpret_cast<u32x4*>(lds_v + swz(r, lc)) = vrow;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -254,6 +334,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       sacc = Mfma<T>::k32(ka, qb[s], sacc);
     }
     float x[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+    if constexpr (kQuant) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= ks;
+    }
     if (tail) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = tok0 + 4 * g + e < my_lim ? x[e] : kNegInf;
@@ -301,8 +385,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       const int chunk = 2 * nb + ((li & 3) >> 1);
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(lds_v3 + swz(tr_row, chunk) + 8 * (li & 1)));
-      o[nb] = Mfma<T>::k16(phi, vb, o[nb]);
-      o[nb] = Mfma<T>::k16(plo, vb, o[nb]);
+      if constexpr (kQuant) {
+        f32x4 t = Mfma<T>::k16(phi, vb, f32x4{0.f, 0.f, 0.f, 0.f});
+        t = Mfma<T>::k16(plo, vb, t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[nb][e] = __builtin_fmaf(vs, t[e], o[nb][e]);
+      } else {
+        o[nb] = Mfma<T>::k16(phi, vb, o[nb]);
+        o[nb] = Mfma<T>::k16(plo, vb, o[nb]);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -312,10 +403,21 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
   // ---- stream: the wave takes pages first + sub, first + sub + wph, ...;
   // each page is kTiles tiles; the next tile's loads are issued before the
   // current tile is computed.
+  // Scales of the page: [page][kv head], read as wave-uniform scalars.
+  auto page_scales = [&](uint32_t pid, float& ks, float& vs) __attribute__((always_inline)) {
+    if constexpr (kQuant) {
+      const int64_t si = static_cast<int64_t>(pid) * Hkv + kvh;
+      ks = p.k_scale[si];
+      vs = p.v_scale[si];
+    }
+  };
   int slot = first + sub;
   if (slot < end) {
-    int64_t base = pt.base(slot);
-    u32x4 kc[kKSteps], vc[kKSteps];
+    uint32_t pid = pt.id(slot);
+    int64_t base = pt.base_of(pid);
+    float ks = 1.f, vs = 1.f;
+    page_scales(pid, ks, vs);
+    u32x4 kc[kLoads], vc[kLoads];
     int t = 0;
     load_tile(base, 0, kc, vc);
     while (true) {
@@ -327,21 +429,28 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       }
       const bool more = nslot < end;
       int64_t nbase = base;
-      u32x4 kn[kKSteps], vn[kKSteps];
+      float nks = ks, nvs = vs;
+      u32x4 kn[kLoads], vn[kLoads];
       if (more) {
-        if (nslot != slot) nbase = pt.base(nslot);
+        if (nslot != slot) {
+          const uint32_t npid = pt.id(nslot);
+          nbase = pt.base_of(npid);
+          page_scales(npid, nks, nvs);
+        }
         load_tile(nbase, nt, kn, vn);
       }
-      consume_tile(tok0, kc, vc);
+      consume_tile(tok0, kc, vc, ks, vs);
       if (!more) break;
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
+      for (int s = 0; s < kLoads; ++s) {
         kc[s] = kn[s];
         vc[s] = vn[s];
       }
       slot = nslot;
       t = nt;
       base = nbase;
+      ks = nks;
+      vs = nvs;
     }
   }
 

@@ -7,14 +7,14 @@
 
 namespace pa {
 
-template <typename T, int D, int PS>
+template <typename T, typename KV, int D, int PS>
 hipError_t launch_attn_mfma_dp(const AttnParams& p, const AttnPlan& plan, int batch,
                                hipStream_t stream) {
   if (plan.waves != kMfmaWaves || plan.rows_per_wg != 16 || kMfmaWaves % plan.heads_per_wg != 0 ||
       p.num_kv_heads % plan.heads_per_wg != 0)
     return hipErrorInvalidValue;
   const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads / plan.heads_per_wg, batch);
-  attn_mfma_kernel<T, D, PS, kMfmaWaves><<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  attn_mfma_kernel<T, KV, D, PS, kMfmaWaves><<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -48,14 +48,39 @@ hipError_t launch_attn_mfma_t(const AttnParams& p, const AttnPlan& plan, int hea
                               int page_size, int batch, hipStream_t stream) {
   if (plan.prefill) return launch_attn_prefill_t<T>(p, plan, head_dim, page_size, batch, stream);
   if (page_size == 16) {
-    if (head_dim == 32) return launch_attn_mfma_dp<T, 32, 16>(p, plan, batch, stream);
-    if (head_dim == 64) return launch_attn_mfma_dp<T, 64, 16>(p, plan, batch, stream);
-    if (head_dim == 128) return launch_attn_mfma_dp<T, 128, 16>(p, plan, batch, stream);
+    if (head_dim == 32) return launch_attn_mfma_dp<T, KvSame, 32, 16>(p, plan, batch, stream);
+    if (head_dim == 64) return launch_attn_mfma_dp<T, KvSame, 64, 16>(p, plan, batch, stream);
+    if (head_dim == 128) return launch_attn_mfma_dp<T, KvSame, 128, 16>(p, plan, batch, stream);
   } else if (page_size == 32) {
-    if (head_dim == 32) return launch_attn_mfma_dp<T, 32, 32>(p, plan, batch, stream);
-    if (head_dim == 64) return launch_attn_mfma_dp<T, 64, 32>(p, plan, batch, stream);
-    if (head_dim == 128) return launch_attn_mfma_dp<T, 128, 32>(p, plan, batch, stream);
+    if (head_dim == 32) return launch_attn_mfma_dp<T, KvSame, 32, 32>(p, plan, batch, stream);
+    if (head_dim == 64) return launch_attn_mfma_dp<T, KvSame, 64, 32>(p, plan, batch, stream);
+    if (head_dim == 128) return launch_attn_mfma_dp<T, KvSame, 128, 32>(p, plan, batch, stream);
   }
+  return hipErrorInvalidValue;
+}
+
+// 8-bit K/V codes: the MFMA kernel only (no shared-tile prefill variant).
+template <typename T, typename KV>
+hipError_t launch_attn_mfma_q_kv(const AttnParams& p, const AttnPlan& plan, int head_dim,
+                                 int page_size, int batch, hipStream_t stream) {
+  if (plan.prefill) return hipErrorInvalidValue;
+  if (page_size == 16) {
+    if (head_dim == 64) return launch_attn_mfma_dp<T, KV, 64, 16>(p, plan, batch, stream);
+    if (head_dim == 128) return launch_attn_mfma_dp<T, KV, 128, 16>(p, plan, batch, stream);
+  } else if (page_size == 32) {
+    if (head_dim == 64) return launch_attn_mfma_dp<T, KV, 64, 32>(p, plan, batch, stream);
+    if (head_dim == 128) return launch_attn_mfma_dp<T, KV, 128, 32>(p, plan, batch, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_attn_mfma_q_t(const AttnParams& p, const AttnPlan& plan, int kv_dtype,
+                                int head_dim, int page_size, int batch, hipStream_t stream) {
+  if (kv_dtype == kI8)
+    return launch_attn_mfma_q_kv<T, KvI8>(p, plan, head_dim, page_size, batch, stream);
+  if (kv_dtype == kFp8E4M3)
+    return launch_attn_mfma_q_kv<T, KvFp8>(p, plan, head_dim, page_size, batch, stream);
   return hipErrorInvalidValue;
 }
 

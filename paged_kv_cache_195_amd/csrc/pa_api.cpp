@@ -41,6 +41,7 @@ int rows_per_wg(int64_t rows_per_kvh) {
 int check_shape(const pa_shape* s, bool decode) {
   if (s == nullptr) return PA_EINVAL;
   if (s->dtype != PA_F32 && s->dtype != PA_F16 && s->dtype != PA_BF16) return PA_EINVAL;
+  if (s->kv_dtype != 0 && s->kv_dtype != PA_I8 && s->kv_dtype != PA_FP8_E4M3) return PA_EINVAL;
   if (s->batch <= 0 || s->seq_q <= 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 ||
       s->head_dim_qk <= 0 || s->head_dim_v <= 0 || s->page_size <= 0 || s->num_pages <= 0 ||
       s->max_pages_per_seq <= 0)
@@ -54,7 +55,7 @@ int check_shape(const pa_shape* s, bool decode) {
   const int64_t rows = static_cast<int64_t>(s->batch) * s->seq_q * s->num_q_heads;
   if (rows > INT32_MAX) return PA_EINVAL;
   // The byte size of one cache tensor must be representable.
-  const int64_t elem = s->dtype == PA_F32 ? 4 : 2;
+  const int64_t elem = s->kv_dtype != 0 ? 1 : (s->dtype == PA_F32 ? 4 : 2);
   const int64_t page_bytes =
       static_cast<int64_t>(s->page_size) * s->num_kv_heads * s->head_dim_qk * elem;
   if (page_bytes > INT32_MAX) return PA_EINVAL;
@@ -68,6 +69,8 @@ int check_shape(const pa_shape* s, bool decode) {
   if ((s->head_dim_qk != 32 && s->head_dim_qk != 64 && s->head_dim_qk != 128) ||
       (s->page_size != 16 && s->page_size != 32))
     return PA_EUNSUPPORTED;
+  // 8-bit caches: 16-bit queries, whole 16-byte code chunks per row lane
+  if (s->kv_dtype != 0 && (s->dtype == PA_F32 || s->head_dim_qk == 32)) return PA_EUNSUPPORTED;
   return PA_OK;
 }
 
@@ -76,8 +79,11 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   const int group = s->num_q_heads / s->num_kv_heads;
   const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
   const int elem = s->dtype == PA_F32 ? 4 : 2;
-  plan.mfma = s->dtype != PA_F32 && rows_per_kvh >= pa::kMfmaMinRows;
-  plan.prefill = plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
+  const bool quant = s->kv_dtype != 0;
+  // 8-bit caches always take the matrix-core kernel (its dequantization to the
+  // operand type is exact); the shared-tile prefill variant reads 16-bit caches
+  plan.mfma = quant || (s->dtype != PA_F32 && rows_per_kvh >= pa::kMfmaMinRows);
+  plan.prefill = !quant && plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
     plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * pa::kPrefillWaves;
@@ -141,9 +147,14 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
   const int32_t* prefix_offset = opt != nullptr ? opt->prefix_offset : nullptr;
   int32_t* page_check = opt != nullptr ? opt->page_check : nullptr;
+  const float* k_scale = opt != nullptr ? opt->k_scale : nullptr;
+  const float* v_scale = opt != nullptr ? opt->v_scale : nullptr;
   if (!aligned4(prefix_offset) || !aligned4(page_check) || !aligned4(seq_lens) ||
-      !aligned4(block_table))
+      !aligned4(block_table) || !aligned4(k_scale) || !aligned4(v_scale))
     return PA_EINVAL;
+  // scales come with 8-bit caches and only with them
+  const bool quant = s->kv_dtype != 0;
+  if (quant != (k_scale != nullptr) || quant != (v_scale != nullptr)) return PA_EINVAL;
 
   const pa::AttnPlan plan = plan_for(s, num_splits);
   const size_t need = workspace_for(s, plan.num_splits);
@@ -157,6 +168,8 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
   p.block_table = block_table;
   p.seq_lens = page_check != nullptr ? page_check + 1 : seq_lens;
   p.prefix_offset = prefix_offset;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.out = out;
   p.lse = lse;
   p.part_out = nullptr;
@@ -186,7 +199,13 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
                                 s->max_pages_per_seq, s->page_size, s->num_pages, page_check, hs);
     if (err != hipSuccess) return PA_EHIP;
   }
-  if (plan.mfma) {
+  if (quant) {
+    err = s->dtype == PA_F16
+              ? pa::launch_attn_mfma_q_f16(p, plan, s->kv_dtype, s->head_dim_qk, s->page_size,
+                                           s->batch, hs)
+              : pa::launch_attn_mfma_q_bf16(p, plan, s->kv_dtype, s->head_dim_qk, s->page_size,
+                                            s->batch, hs);
+  } else if (plan.mfma) {
     err = s->dtype == PA_F16
               ? pa::launch_attn_mfma_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs)
               : pa::launch_attn_mfma_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);

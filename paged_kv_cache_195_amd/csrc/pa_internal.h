@@ -15,6 +15,8 @@ struct AttnParams {
   const int32_t* block_table;  // row b at block_table + b * bt_stride
   const int32_t* seq_lens;     // [B]
   const int32_t* prefix_offset;  // [B] key position of each sequence's row 0, or nullptr
+  const float* k_scale;        // [num_pages, Hkv] for 8-bit caches, else nullptr
+  const float* v_scale;        // [num_pages, Hkv] for 8-bit caches, else nullptr
   void* out;                   // [B, Sq, Hq, Dv]           (num_splits == 1)
   float* lse;                  // [B, Sq, Hq] or nullptr     (num_splits == 1)
   float* part_out;             // [B*Sq*Hq, S, Dv]           (num_splits > 1)
@@ -68,7 +70,7 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowBlocks = 2;
 constexpr int kPrefillMinRows = 64;
 
-enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFp8E4M3 = 4 };
 
 // Grid = (S * row_groups, Hkv, B); returns a hipError_t.
 hipError_t launch_attn_valu_f32(const AttnParams& p, const AttnPlan& plan, int head_dim,
@@ -91,6 +93,13 @@ hipError_t launch_attn_mfma_bf16(const AttnParams& p, const AttnPlan& plan, int 
 hipError_t launch_page_check(const int32_t* block_table, int64_t bt_stride,
                              const int32_t* seq_lens, int batch, int width, int page_size,
                              int64_t num_pages, int32_t* result, hipStream_t stream);
+
+// The MFMA kernel over 8-bit K/V codes (kv_dtype PA_I8 or PA_FP8_E4M3), q and
+// out of the named type; D in {64, 128}.
+hipError_t launch_attn_mfma_q_f16(const AttnParams& p, const AttnPlan& plan, int kv_dtype,
+                                  int head_dim, int page_size, int batch, hipStream_t stream);
+hipError_t launch_attn_mfma_q_bf16(const AttnParams& p, const AttnPlan& plan, int kv_dtype,
+                                   int head_dim, int page_size, int batch, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,

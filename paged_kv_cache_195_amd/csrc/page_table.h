@@ -28,12 +28,17 @@ struct PageTable {
   int64_t page_bytes;   // bytes of one page of one cache tensor
   int n_pages;          // ceil(seq_len / page_size): slots that may be read
 
-  // Byte offset of the page in slot `slot` from the start of the cache.
-  // The caller guarantees 0 <= slot < n_pages; `slot` is wave-uniform.
-  __device__ __forceinline__ int64_t base(int slot) const {
-    const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(row[slot]));
-    return static_cast<int64_t>(static_cast<uint64_t>(id)) * page_bytes;
+  // Physical page id in slot `slot`, wave-uniform.  The caller guarantees
+  // 0 <= slot < n_pages; `slot` is wave-uniform.
+  __device__ __forceinline__ uint32_t id(int slot) const {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(row[slot]));
   }
+  // Byte offset of page `page_id` from the start of the cache.
+  __device__ __forceinline__ int64_t base_of(uint32_t page_id) const {
+    return static_cast<int64_t>(static_cast<uint64_t>(page_id)) * page_bytes;
+  }
+  // Byte offset of the page in slot `slot` from the start of the cache.
+  __device__ __forceinline__ int64_t base(int slot) const { return base_of(id(slot)); }
 };
 
 }  // namespace pa

@@ -44,6 +44,15 @@ Workloads (``WORKLOADS``):
                     page 16.
 ``prefill_b1_s4096``  causal prefill bf16, B=1, Sq=L=4096, Hq=64, Hkv=8, D=128,
                     page 16.
+``llama3_8b_decode_int8`` / ``llama3_8b_decode_fp8``  the Llama-3-8B decode
+                    shape with 8-bit K/V codes (1 GiB per cache).
+
+8-bit caches (``kv="int8"`` or ``kv="fp8_e4m3"``): K and V hold codes drawn
+from the same seeded normals -- int8 as round(32 x) clamped to [-127, 127],
+fp8 as torch's float8_e4m3fn conversion of x -- with one float32 scale per
+(page, kv head) drawn uniform in [0.5, 1.5) (divided by 32 for int8).
+Unreferenced pages get NaN scales and poison codes (fp8: the NaN code; int8:
+-128, which the generator never produces), last-page tails poison codes.
 """
 
 from __future__ import annotations
@@ -73,6 +82,7 @@ class WorkloadSpec:
     splits: tuple
     seed: int
     description: str
+    kv: Optional[str] = None      # None, "int8" or "fp8_e4m3": 8-bit K/V codes
 
 
 WORKLOADS = {
@@ -101,7 +111,17 @@ WORKLOADS = {
     "prefill_b1_s4096": WorkloadSpec("prefill_b1_s4096", "bf16", 1, 4096, 64, 8, 128, 16, True,
                                      (0,), 8,
                                      "causal prefill bf16 B=1 Sq=L=4096 Hq=64 Hkv=8 D=128 page16"),
+    "llama3_8b_decode_int8": WorkloadSpec("llama3_8b_decode_int8", "bf16", 256, 1, 32, 8, 128, 16,
+                                          False, (0,), 9,
+                                          "Llama-3-8B decode, int8 K/V codes, bf16 q/out B=256 "
+                                          "Hq=32 Hkv=8 D=128 page16 Skv=4096", "int8"),
+    "llama3_8b_decode_fp8": WorkloadSpec("llama3_8b_decode_fp8", "bf16", 256, 1, 32, 8, 128, 16,
+                                         False, (0,), 10,
+                                         "Llama-3-8B decode, fp8 E4M3 K/V codes, bf16 q/out B=256 "
+                                         "Hq=32 Hkv=8 D=128 page16 Skv=4096", "fp8_e4m3"),
 }
+
+KV_KINDS = ("int8", "fp8_e4m3")
 
 WORKLOAD_ORDER = ["tiny_f32", "prefill_f16", "ragged_bf16", "llama3_8b_decode", "qwen3_235b_decode"]
 
@@ -122,6 +142,9 @@ class PagedInputs:
     seq_lens_host: List[int] = field(default_factory=list)
     table_host: Optional[torch.Tensor] = None   # CPU int32 copy of block_table
     notes: dict = field(default_factory=dict)
+    kv: Optional[str] = None                    # 8-bit code kind of the caches, or None
+    k_scale: Optional[torch.Tensor] = None      # [num_pages, Hkv] float32 (8-bit caches)
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def batch(self) -> int:
@@ -130,6 +153,53 @@ class PagedInputs:
 
 def _normal(gen, shape, dtype, device):
     return torch.randn(shape, generator=gen, dtype=torch.float32, device=device).to(dtype)
+
+
+def _codes(gen, shape, kind, device):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    if kind == "int8":
+        return torch.clamp(torch.round(x * 32.0), -127.0, 127.0).to(torch.int8)
+    if kind == "fp8_e4m3":
+        return x.to(torch.float8_e4m3fn)
+    raise ValueError(kind)
+
+
+def _scales(gen, shape, kind, device):
+    u = torch.rand(shape, generator=gen, dtype=torch.float32, device=device) + 0.5
+    return u / 32.0 if kind == "int8" else u
+
+
+POISON_CODE = {"int8": 0x80, "fp8_e4m3": 0x7F}
+
+
+def _poison_codes(codes: torch.Tensor, scales: torch.Tensor, kind: str, used_pages: torch.Tensor,
+                  lens: List[int], table: torch.Tensor, page_size: int):
+    """Poison codes and NaN scales in unreferenced pages; poison codes past each
+    sequence's end."""
+    raw = codes.view(torch.uint8)
+    mask = torch.ones(codes.shape[0], dtype=torch.bool, device=codes.device)
+    mask[used_pages.long()] = False
+    raw[mask] = POISON_CODE[kind]
+    scales[mask] = float("nan")
+    for b, seq_len in enumerate(lens):
+        n = -(-seq_len // page_size)
+        tail = n * page_size - seq_len
+        if n and tail:
+            raw[int(table[b, n - 1])][page_size - tail:] = POISON_CODE[kind]
+
+
+def _quantize_inputs(inputs, gen, kind, used, lens, table, poison):
+    """Replace the float caches of ``inputs`` by 8-bit codes and scales."""
+    phys, ps, hkv, d = inputs.k_cache.shape
+    device = inputs.k_cache.device
+    inputs.k_cache = _codes(gen, (phys, ps, hkv, d), kind, device)
+    inputs.v_cache = _codes(gen, (phys, ps, hkv, d), kind, device)
+    inputs.k_scale = _scales(gen, (phys, hkv), kind, device)
+    inputs.v_scale = _scales(gen, (phys, hkv), kind, device)
+    inputs.kv = kind
+    if poison:
+        _poison_codes(inputs.k_cache, inputs.k_scale, kind, used, lens, table, ps)
+        _poison_codes(inputs.v_cache, inputs.v_scale, kind, used, lens, table, ps)
 
 
 def _poison_unused(cache: torch.Tensor, used_pages: torch.Tensor, lens: List[int],
@@ -149,7 +219,7 @@ def _poison_unused(cache: torch.Tensor, used_pages: torch.Tensor, lens: List[int
 
 def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: Optional[str] = None,
                   seq_lens: Optional[List[int]] = None, batch: Optional[int] = None,
-                  table_stride: Optional[int] = None) -> PagedInputs:
+                  table_stride: Optional[int] = None, kv: Optional[str] = None) -> PagedInputs:
     """Build the named workload on ``device``.
 
     ``seed`` defaults to the workload's own.  ``variant`` selects a variant
@@ -157,9 +227,13 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
     order on the two large decode shapes).  ``seq_lens``/``batch`` override the
     lengths (tests use this for edge cases on the small workloads).
     ``table_stride`` reads the block table through a row stride larger than
-    its width.
+    its width.  ``kv`` ("int8" or "fp8_e4m3") stores K and V as 8-bit codes
+    (the ``*_int8`` / ``*_fp8`` workloads set it themselves).
     """
     spec = WORKLOADS[name]
+    kv = spec.kv if kv is None else kv
+    if spec.kv is not None:
+        name = name.rsplit("_", 1)[0]
     seed = spec.seed if seed is None else seed
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -245,6 +319,12 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
                          seq_lens=seq_lens_t, scale=1.0 / math.sqrt(d), causal=spec.causal,
                          num_pages_arg=num_pages_arg, seq_lens_host=list(lens),
                          table_host=table.cpu())
+    if kv is not None:
+        del k_cache, v_cache
+        inputs.k_cache = inputs.v_cache = None
+        inputs.k_cache = torch.empty((phys, ps, hkv, d), dtype=torch.int8, device=device)
+        _quantize_inputs(inputs, gen, kv, used, lens, table,
+                         poison=name in ("tiny_f32", "ragged_bf16", "prefill_f16"))
     inputs.notes["true_num_pages"] = phys
     inputs.notes["table_storage"] = storage
     inputs.notes["variant"] = variant
@@ -272,15 +352,21 @@ def kv_bytes(inputs: PagedInputs) -> int:
     L tokens of each sequence, once, for K and for V."""
     spec = inputs.spec
     per_token = spec.num_kv_heads * spec.head_dim * inputs.k_cache.element_size()
-    return 2 * per_token * sum(inputs.seq_lens_host)
+    total = 2 * per_token * sum(inputs.seq_lens_host)
+    if inputs.kv is not None:   # one K and one V float32 scale per (page, kv head) read
+        ps = inputs.k_cache.shape[1]
+        total += 2 * 4 * spec.num_kv_heads * sum(-(-x // ps) for x in inputs.seq_lens_host)
+    return total
 
 
 def make_custom(dtype: str, seq_lens: List[int], num_q_heads: int, num_kv_heads: int,
                 head_dim: int, page_size: int, seq_q: int = 1, causal: bool = False,
                 width: Optional[int] = None, extra_pages: int = 5, seed: int = 0,
-                device="cpu", table_stride: Optional[int] = None) -> PagedInputs:
+                device="cpu", table_stride: Optional[int] = None,
+                kv: Optional[str] = None) -> PagedInputs:
     """Any shape, same recipe as the named workloads (shuffled pages, unmapped
-    unused slots, NaN in unreferenced pages and in last-page tails)."""
+    unused slots, NaN in unreferenced pages and in last-page tails); ``kv``
+    stores K and V as 8-bit codes with per-(page, kv head) scales."""
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     tdtype = DTYPES[dtype]
@@ -315,4 +401,6 @@ def make_custom(dtype: str, seq_lens: List[int], num_q_heads: int, num_kv_heads:
                          seq_lens_host=list(seq_lens), table_host=table.cpu())
     inputs.notes["true_num_pages"] = phys
     inputs.notes["table_storage"] = storage
+    if kv is not None:
+        _quantize_inputs(inputs, gen, kv, used, list(seq_lens), table, poison=True)
     return inputs
