@@ -33,16 +33,27 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA peaks
 TRAFFIC_FILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_traffic.md"),
     "qwen3_235b_decode": os.path.join(ROOT, "profiles", "attn_decode_qwen3_235b_traffic.md"),
+    "llama3_8b_decode_int8": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_int8_traffic.md"),
+    "llama3_8b_decode_fp8": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_fp8_traffic.md"),
 }
 KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
+# the sources each workload's kernel is built from (host planning included)
+_COMMON = ["device_common.h", "page_table.h", "pa_internal.h", "pa_api.cpp"]
+_MFMA = ["attn_mfma.h", "attn_mfma_launch.h", "attn_prefill.h"]
+TRAFFIC_SOURCES = {
+    "llama3_8b_decode": _COMMON + ["attn_valu.h", "attn_valu_launch.h", "attn_valu_bf16.hip"],
+    "qwen3_235b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
+    "llama3_8b_decode_int8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],
+    "llama3_8b_decode_fp8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
+    """sha256 over the sources the workload's kernel is built from."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".h", ".hip", ".cpp")):
-            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(TRAFFIC_SOURCES[workload]):
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -54,7 +65,7 @@ def measured_traffic(workload: str = "llama3_8b_decode"):
         return None
     text = open(path).read()
     fields = dict(re.findall(r"^\s*[-*]?\s*`?(\w+)`?\s*[:=]\s*`?([0-9a-f.e+]+)`?\s*$", text, re.M))
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(workload):
         return None
     try:
         return int(float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"]))
@@ -79,16 +90,28 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
         if b not in order:
             order.append(b)
 
-    def host_pages(cache, rows):
+    def host_pages(cache, scales, rows):
+        """Host copies of the pages ``rows`` reference.  8-bit pages stay codes
+        here; the oracle dequantizes each page when the gather reads it, inside
+        the timed work."""
         ids = sorted({int(x) for b in rows for x in w.table_host[b, : -(-w.seq_lens_host[b] // ps)]})
-        pages = cache.index_select(0, torch.tensor(ids, device=cache.device)).float().cpu().numpy()
-        lut = {pid: pages[i] for i, pid in enumerate(ids)}
+        idx = torch.tensor(ids, device=cache.device)
+        if w.kv is None:
+            pages = cache.index_select(0, idx).float().cpu().numpy()
+            page_scales = None
+        else:
+            pages = cache.view(torch.uint8).index_select(0, idx).cpu().numpy()
+            page_scales = scales.index_select(0, idx).cpu().numpy()
+        lut = {pid: i for i, pid in enumerate(ids)}
 
         class Pages:
             shape = tuple(cache.shape)
 
             def __getitem__(self, pid):
-                return lut[int(pid)]
+                i = lut[int(pid)]
+                if page_scales is None:
+                    return pages[i]
+                return O.dequantize_cache(pages[i:i + 1], page_scales[i:i + 1], w.kv)[0]
         return Pages()
 
     def one(b, kp, vp):
@@ -96,11 +119,11 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
                            w.table_host[b:b + 1].numpy(), np.array(w.seq_lens_host[b:b + 1]),
                            w.scale, w.causal)
 
-    done, elapsed, max_err, tokens = [], 0.0, 0.0, 0
+    done, elapsed, max_err, tokens, pages_read = [], 0.0, 0.0, 0, 0
     with threadpool_limits(limits=1):
         while elapsed < budget_s and len(done) < batch:
             rows = order[len(done): len(done) + threads]
-            kp, vp = host_pages(w.k_cache, rows), host_pages(w.v_cache, rows)
+            kp, vp = host_pages(w.k_cache, w.k_scale, rows), host_pages(w.v_cache, w.v_scale, rows)
             t0 = time.perf_counter()
             with cf.ThreadPoolExecutor(max_workers=threads) as ex:
                 res = list(ex.map(lambda b: one(b, kp, vp), rows))
@@ -109,10 +132,14 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
                 y = out_gpu[b].float().cpu().numpy()
                 max_err = max(max_err, float(np.abs(y - xo[0, 0]).max()))
                 tokens += w.seq_lens_host[b]
+                pages_read += -(-w.seq_lens_host[b] // ps)
             done.extend(rows)
     per_token = 2 * w.k_cache.shape[2] * w.k_cache.shape[3] * w.k_cache.element_size()
+    nbytes = tokens * per_token
+    if w.kv is not None:   # the K and V scales of every page read
+        nbytes += 2 * 4 * w.k_cache.shape[2] * pages_read
     return {
-        "value": round(tokens * per_token / elapsed / 1e9, 4),
+        "value": round(nbytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
@@ -146,13 +173,17 @@ def copy_calibration(mib: int, steps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # ~35-70 ms of untimed steps: after input generation the GPU needs some
+    # milliseconds of load to reach steady clocks (5 steps: 403 us, 100 steps:
+    # 344 us per int8 step)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--splits", type=int, default=0, help="split-KV count (0 = automatic)")
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "qwen3_235b_decode", "llama3_70b_decode",
                              "decode_b64_s8192_g8", "ragged_bf16", "tiny_f32",
-                             "prefill_b4_s1024", "prefill_b1_s4096", "prefill_f16"],
+                             "prefill_b4_s1024", "prefill_b1_s4096", "prefill_f16",
+                             "llama3_8b_decode_int8", "llama3_8b_decode_fp8"],
                     help="decode workload (the metric is quoted on llama3_8b_decode)")
     ap.add_argument("--variant", default=None,
                     help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "
@@ -197,7 +228,8 @@ def main():
     def step():
         fn = pa.prefill if prefill else pa.decode
         fn(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale, causal=w.causal,
-           num_splits=args.splits, out=out, lse=lse, workspace=workspace)
+           num_splits=args.splits, out=out, lse=lse, workspace=workspace, k_scale=w.k_scale,
+           v_scale=w.v_scale)
 
     for _ in range(args.warmup):
         step()
@@ -269,6 +301,8 @@ def main():
             "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
             "head_dim": spec.head_dim, "page_size": spec.page_size, "num_splits": splits,
             "page_order": args.variant or "random",
+            "kv_cache": (f"{w.kv} codes + float32 scale per (page, kv head)" if w.kv
+                         else spec.dtype),
             "kv_bytes_per_step": nbytes,
             "graph": args.graph,
         },

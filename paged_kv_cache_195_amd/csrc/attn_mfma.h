@@ -51,6 +51,12 @@
 #include "pa_internal.h"
 #include "page_table.h"
 
+// Tiles in flight ahead of the compute, per wave, for 8-bit caches (a
+// compile-time tuning constant; 16-bit caches run one tile ahead).
+#ifndef PA_QUANT_AHEAD
+#define PA_QUANT_AHEAD 3
+#endif
+
 namespace pa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -400,10 +406,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- stream: the wave takes pages first + sub, first + sub + wph, ...;
-  // each page is kTiles tiles; the next tile's loads are issued before the
-  // current tile is computed.
-  // Scales of the page: [page][kv head], read as wave-uniform scalars.
+  // Scales of a page: [page][kv head], read as wave-uniform scalars.
   auto page_scales = [&](uint32_t pid, float& ks, float& vs) __attribute__((always_inline)) {
     if constexpr (kQuant) {
       const int64_t si = static_cast<int64_t>(pid) * Hkv + kvh;
@@ -411,46 +414,87 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       vs = p.v_scale[si];
     }
   };
-  int slot = first + sub;
-  if (slot < end) {
-    uint32_t pid = pt.id(slot);
-    int64_t base = pt.base_of(pid);
-    float ks = 1.f, vs = 1.f;
-    page_scales(pid, ks, vs);
-    u32x4 kc[kLoads], vc[kLoads];
-    int t = 0;
-    load_tile(base, 0, kc, vc);
-    while (true) {
-      const int tok0 = slot * PS + 16 * t;
-      int nslot = slot, nt = t + 1;
-      if (nt == kTiles) {
-        nslot = slot + wph;
-        nt = 0;
-      }
-      const bool more = nslot < end;
-      int64_t nbase = base;
-      float nks = ks, nvs = vs;
-      u32x4 kn[kLoads], vn[kLoads];
-      if (more) {
-        if (nslot != slot) {
-          const uint32_t npid = pt.id(nslot);
-          nbase = pt.base_of(npid);
-          page_scales(npid, nks, nvs);
+  if constexpr (!kQuant) {
+    // ---- stream, 16-bit caches: the wave takes pages first + sub,
+    // first + sub + wph, ...; each page is kTiles tiles; the next tile's
+    // loads are issued before the current tile is computed.
+    int slot = first + sub;
+    if (slot < end) {
+      int64_t base = pt.base(slot);
+      u32x4 kc[kLoads], vc[kLoads];
+      int t = 0;
+      load_tile(base, 0, kc, vc);
+      while (true) {
+        const int tok0 = slot * PS + 16 * t;
+        int nslot = slot, nt = t + 1;
+        if (nt == kTiles) {
+          nslot = slot + wph;
+          nt = 0;
         }
-        load_tile(nbase, nt, kn, vn);
-      }
-      consume_tile(tok0, kc, vc, ks, vs);
-      if (!more) break;
+        const bool more = nslot < end;
+        int64_t nbase = base;
+        u32x4 kn[kLoads], vn[kLoads];
+        if (more) {
+          if (nslot != slot) nbase = pt.base(nslot);
+          load_tile(nbase, nt, kn, vn);
+        }
+        consume_tile(tok0, kc, vc, 1.f, 1.f);
+        if (!more) break;
 #pragma unroll
-      for (int s = 0; s < kLoads; ++s) {
-        kc[s] = kn[s];
-        vc[s] = vn[s];
+        for (int s = 0; s < kLoads; ++s) {
+          kc[s] = kn[s];
+          vc[s] = vn[s];
+        }
+        slot = nslot;
+        t = nt;
+        base = nbase;
       }
-      slot = nslot;
-      t = nt;
-      base = nbase;
-      ks = nks;
-      vs = nvs;
+    }
+  } else {
+    // ---- stream, 8-bit caches: the same tile order (tile k is tile
+    // k % kTiles of the page in slot first + sub + (k / kTiles) * wph), with
+    // loads kAhead tiles ahead of the compute through a ring of kAhead + 1
+    // register buffers indexed by compile-time stages.  An 8-bit tile holds
+    // half the bytes of a 16-bit one, so more of them stay in flight (one
+    // ahead: 452 us, three ahead: 356 us on the Llama-3-8B decode shape).
+    constexpr int kAhead = PA_QUANT_AHEAD;
+    constexpr int kRing = kAhead + 1;
+    const int my_first = first + sub;
+    const int my_pages = my_first < end ? (end - my_first + wph - 1) / wph : 0;
+    const int n_tiles = my_pages * kTiles;
+    u32x4 kr[kRing][kLoads], vr[kRing][kLoads];
+    float rks[kRing], rvs[kRing];
+    int64_t cur_base = 0;
+    float cur_ks = 1.f, cur_vs = 1.f;
+    // issue the loads of tile k into one ring stage
+    auto issue = [&](int k, u32x4* kk, u32x4* vv, float& ks, float& vs)
+                     __attribute__((always_inline)) {
+      const int pg = k / kTiles;
+      const int t = k - pg * kTiles;
+      if (t == 0) {
+        const uint32_t pid = pt.id(my_first + pg * wph);
+        cur_base = pt.base_of(pid);
+        page_scales(pid, cur_ks, cur_vs);
+      }
+      ks = cur_ks;
+      vs = cur_vs;
+      load_tile(cur_base, t, kk, vv);
+    };
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st)
+      if (st < n_tiles) issue(st, kr[st], vr[st], rks[st], rvs[st]);
+    for (int k0 = 0; k0 < n_tiles; k0 += kRing) {
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) {
+        const int k = k0 + st;
+        if (k < n_tiles) {  // wave-uniform
+          const int ns = (st + kAhead) % kRing;
+          if (k + kAhead < n_tiles) issue(k + kAhead, kr[ns], vr[ns], rks[ns], rvs[ns]);
+          const int pg = k / kTiles;
+          const int tok0 = (my_first + pg * wph) * PS + 16 * (k - pg * kTiles);
+          consume_tile(tok0, kr[st], vr[st], rks[st], rvs[st]);
+        }
+      }
     }
   }
 
