@@ -41,7 +41,7 @@ KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
 _COMMON = ["device_common.h", "page_table.h", "pa_internal.h", "pa_api.cpp"]
 _MFMA = ["attn_mfma.h", "attn_mfma_launch.h", "attn_prefill.h"]
 TRAFFIC_SOURCES = {
-    "llama3_8b_decode": _COMMON + ["attn_valu.h", "attn_valu_launch.h", "attn_valu_bf16.hip"],
+    "llama3_8b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
     "qwen3_235b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
     "llama3_8b_decode_int8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],
     "llama3_8b_decode_fp8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],

@@ -26,8 +26,6 @@ ARCH = "gfx950"
 SOURCES = [
     "pa_api.cpp",
     "attn_valu_f32.hip",
-    "attn_valu_f16.hip",
-    "attn_valu_bf16.hip",
     "attn_mfma_f16.hip",
     "attn_mfma_bf16.hip",
     "attn_mfma_q_f16.hip",

@@ -80,9 +80,10 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   const int64_t rows_per_kvh = static_cast<int64_t>(s->seq_q) * group;
   const int elem = s->dtype == PA_F32 ? 4 : 2;
   const bool quant = s->kv_dtype != 0;
-  // 8-bit caches always take the matrix-core kernel (its dequantization to the
-  // operand type is exact); the shared-tile prefill variant reads 16-bit caches
-  plan.mfma = quant || (s->dtype != PA_F32 && rows_per_kvh >= pa::kMfmaMinRows);
+  // 16-bit and 8-bit caches take the matrix-core kernels (8-bit codes are
+  // dequantized exactly to the operand type); f32 caches the vector-ALU one.
+  // The shared-tile prefill variant reads 16-bit caches.
+  plan.mfma = quant || s->dtype != PA_F32;
   plan.prefill = !quant && plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
@@ -210,17 +211,7 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
               ? pa::launch_attn_mfma_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs)
               : pa::launch_attn_mfma_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
   } else {
-    switch (s->dtype) {
-      case PA_F32:
-        err = pa::launch_attn_valu_f32(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-        break;
-      case PA_F16:
-        err = pa::launch_attn_valu_f16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-        break;
-      default:
-        err = pa::launch_attn_valu_bf16(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
-        break;
-    }
+    err = pa::launch_attn_valu_f32(p, plan, s->head_dim_qk, s->page_size, s->batch, hs);
   }
   if (err != hipSuccess) return PA_EHIP;
   if (plan.num_splits > 1) {

@@ -35,7 +35,7 @@ struct AttnParams {
 
 // Launch shape chosen on the host.
 struct AttnPlan {
-  bool mfma;         // matrix-core kernel (16-bit caches, >= 8 rows per kv head)
+  bool mfma;         // matrix-core kernel (16-bit and 8-bit caches)
   bool prefill;      // the shared-tile prefill variant of it (>= 64 rows per kv head)
   int rows_per_wg;   // MR: query rows (position, head) per kv head in one workgroup
   int row_groups;    // ceil(rows_per_kvh / MR)
@@ -61,9 +61,13 @@ constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, in
                                                                               : ValuConfig{8, 0};
 }
 
-// The matrix-core kernel: 16 rows per kv head and workgroup, 8 waves.
+// The matrix-core kernel: 16 rows per kv head and workgroup, 8 waves.  It
+// serves every 16-bit and 8-bit cache (the shared-tile prefill kernel aside):
+// even at 1, 2 or 4 query rows per kv head, where most of its 16-row tile is
+// padding, it streams faster than the vector-ALU kernel (bf16 decode, B=256,
+// Skv 4096, 8 kv heads: 620 against 650-685 us at G = 4, 622 against 639 us
+// at G = 1), which is left to f32 caches.
 constexpr int kMfmaWaves = 8;
-constexpr int kMfmaMinRows = 8;
 // The shared-tile prefill kernel: kPrefillRowBlocks blocks of 16 rows per
 // wave, kPrefillWaves waves, one kv head per workgroup; D in {64, 128}.
 constexpr int kPrefillWaves = 4;
@@ -75,10 +79,6 @@ enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFp8E4M3 = 4 };
 // Grid = (S * row_groups, Hkv, B); returns a hipError_t.
 hipError_t launch_attn_valu_f32(const AttnParams& p, const AttnPlan& plan, int head_dim,
                                 int page_size, int batch, hipStream_t stream);
-hipError_t launch_attn_valu_f16(const AttnParams& p, const AttnPlan& plan, int head_dim,
-                                int page_size, int batch, hipStream_t stream);
-hipError_t launch_attn_valu_bf16(const AttnParams& p, const AttnPlan& plan, int head_dim,
-                                 int page_size, int batch, hipStream_t stream);
 
 
 hipError_t launch_attn_mfma_f16(const AttnParams& p, const AttnPlan& plan, int head_dim,
