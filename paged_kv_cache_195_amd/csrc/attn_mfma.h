@@ -178,6 +178,14 @@ __device__ __forceinline__ void widen16(const u32x4& w, u32x4& lo, u32x4& hi) {
 // of 16); NW: waves per workgroup.  p.heads_per_wg kv heads per workgroup,
 // NW / heads_per_wg waves per head; each workgroup covers 16 rows per kv head
 // (row group rg = blockIdx.x / S).
+// Static LDS of one workgroup: per wave, a K and a V tile of 16 staged rows,
+// reused for the final merge.
+template <int D, int NW>
+constexpr int mfma_static_lds() {
+  return NW * ((2 * 16 * D * 2) > (16 * D * 4 + 2 * 16 * 4) ? (2 * 16 * D * 2)
+                                                            : (16 * D * 4 + 2 * 16 * 4));
+}
+
 template <typename T, typename KV, int D, int PS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) {
   static_assert(D % 32 == 0 && PS % 16 == 0, "tile shape");
@@ -280,6 +288,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
   constexpr int kTileLds = 2 * 16 * kRowBytes;
   constexpr int kMergeLds = 16 * D * 4 + 2 * 16 * 4;
   constexpr int kPerWave = kTileLds > kMergeLds ? kTileLds : kMergeLds;
+  static_assert(NW * kPerWave == mfma_static_lds<D, NW>(), "LDS size");
   __shared__ __attribute__((aligned(16))) char smem[NW * kPerWave];
   char* my_lds = smem + wave * kPerWave;
   lds_char* my_lds3 = (lds_char*)(smem) + wave * kPerWave;

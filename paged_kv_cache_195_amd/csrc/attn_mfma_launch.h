@@ -7,15 +7,35 @@
 
 namespace pa {
 
-template <typename T, typename KV, int D, int PS>
-hipError_t launch_attn_mfma_dp(const AttnParams& p, const AttnPlan& plan, int batch,
-                               hipStream_t stream) {
-  if (plan.waves != kMfmaWaves || plan.rows_per_wg != 16 || kMfmaWaves % plan.heads_per_wg != 0 ||
+template <typename T, typename KV, int D, int PS, int NW>
+hipError_t launch_attn_mfma_dpw(const AttnParams& p, const AttnPlan& plan, int batch,
+                                hipStream_t stream) {
+  if (plan.rows_per_wg != 16 || NW % plan.heads_per_wg != 0 ||
       p.num_kv_heads % plan.heads_per_wg != 0)
     return hipErrorInvalidValue;
   const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads / plan.heads_per_wg, batch);
-  attn_mfma_kernel<T, KV, D, PS, kMfmaWaves><<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  // 4-wave workgroups reserve unused LDS so that two, not three, stay resident
+  // per compute unit: 8 waves per CU, as with 8-wave workgroups.  At 12 resident
+  // waves the Qwen3-235B decode step took 726 us instead of 632.
+  constexpr int kStatic = mfma_static_lds<D, NW>();
+  constexpr size_t kReserve = NW == 4 && kStatic < kMfmaLdsPerNarrowWg
+                                  ? static_cast<size_t>(kMfmaLdsPerNarrowWg - kStatic)
+                                  : 0;
+  attn_mfma_kernel<T, KV, D, PS, NW><<<grid, dim3(NW * 64), kReserve, stream>>>(p);
   return hipGetLastError();
+}
+
+// 16-bit caches: 8 or 4 waves per workgroup; 8-bit codes: 8.
+template <typename T, typename KV, int D, int PS>
+hipError_t launch_attn_mfma_dp(const AttnParams& p, const AttnPlan& plan, int batch,
+                               hipStream_t stream) {
+  if (plan.waves == kMfmaWaves)
+    return launch_attn_mfma_dpw<T, KV, D, PS, kMfmaWaves>(p, plan, batch, stream);
+  if constexpr (!KvTraits<KV>::quant) {
+    if (plan.waves == kMfmaWavesNarrow)
+      return launch_attn_mfma_dpw<T, KV, D, PS, kMfmaWavesNarrow>(p, plan, batch, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D, int PS>

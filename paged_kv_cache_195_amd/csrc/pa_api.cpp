@@ -91,7 +91,7 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
     plan.waves = pa::kPrefillWaves;
   } else if (plan.mfma) {
     plan.rows_per_wg = 16;
-    plan.waves = pa::kMfmaWaves;
+    plan.waves = (!quant && s->num_kv_heads % 8 != 0) ? pa::kMfmaWavesNarrow : pa::kMfmaWaves;
   } else {
     plan.rows_per_wg = rows_per_wg(rows_per_kvh);
     plan.waves = pa::valu_config(elem, s->head_dim_qk, s->page_size, plan.rows_per_wg).waves;

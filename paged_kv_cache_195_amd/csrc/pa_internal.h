@@ -67,7 +67,19 @@ constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, in
 // padding, it streams faster than the vector-ALU kernel (bf16 decode, B=256,
 // Skv 4096, 8 kv heads: 620 against 650-685 us at G = 4, 622 against 639 us
 // at G = 1), which is left to f32 caches.
+//
+// Waves per workgroup: 8, or 4 for 16-bit caches whose kv-head count is not a
+// multiple of 8.  The fastest layout gives each kv head of a page one wave and
+// lets one workgroup cover all kv heads of its pages (Qwen3-235B decode,
+// Hkv = 4: 632 against 638 us; Hkv = 4, G = 4: 623 against 633 us); at
+// Hkv = 8 eight waves win (Llama-3-8B decode 621 against 627 us).  8-bit
+// caches keep 8 (the int8 step ran 352 against 371 us with 4).  Both widths
+// run 8 resident waves per compute unit: more resident waves stream slower.
 constexpr int kMfmaWaves = 8;
+constexpr int kMfmaWavesNarrow = 4;
+// LDS a 4-wave workgroup holds (static plus reserved): more than a third of a
+// compute unit's 160 KiB, so at most two are resident.
+constexpr int kMfmaLdsPerNarrowWg = 56 * 1024;
 // The shared-tile prefill kernel: kPrefillRowBlocks blocks of 16 rows per
 // wave, kPrefillWaves waves, one kv head per workgroup; D in {64, 128}.
 constexpr int kPrefillWaves = 4;
