@@ -38,13 +38,14 @@
 // a zero weight in the MFMA.
 //
 // Quantized caches (8-bit codes, one float32 scale per (page, kv head)): each
-// lane loads 16 codes of a row, decodes them to float (int8: one SDWA
-// convert per code; fp8 E4M3: one v_cvt_pk_f32_fp8 per two codes, which
-// decodes the OCP format on gfx950) and packs them to the 16-bit operand
-// type, exactly (a code has at most 8 significant bits, inside the range of
-// both types).  The staged rows then feed the same MFMA steps.  The K scale
+// lane loads 16 codes of a row and decodes them exactly to the 16-bit operand
+// type (int8: one SDWA convert to float per code, then the top halves or a
+// round-toward-zero pack, exact since a code has at most 8 significant bits;
+// fp8 E4M3: one gfx950 scaled conversion per two codes, straight to the
+// operand type, which decodes the OCP format).  The staged rows then feed the same MFMA steps.  The K scale
 // multiplies the tile's scores; the V scale multiplies the tile's P.V product
-// before it is added to O, so a scale of any sign or size costs no precision.
+// before it is added to O (with bf16 operands it folds into the weights
+// instead), so a scale of any sign or size costs no precision.
 #pragma once
 
 #include "device_common.h"
@@ -113,7 +114,7 @@ struct Mfma<bf16_t> {
   static __device__ __forceinline__ f32x4 k16(s16x4 a, s16x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
   }
-  // Two weights a, b (finite, >= 0) as packed high and low parts:
+  // Two finite weights a, b (of either sign) as packed high and low parts:
   // hi = the top 16 bits of each (exact as floats), lo = bf16(p - hi) rounded
   // to nearest even, so hi + lo keeps about 16 significant bits.
   static __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
@@ -157,16 +158,33 @@ struct Mfma<f16_t> {
   }
 };
 
+// Two fp8 E4M3 codes (the low or the high half of a word) as a packed pair of
+// the operand type, in one gfx950 scaled conversion with scale 1 (exact; all
+// 256 codes were checked against the format on the GPU).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8_pair(bf16_t, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8_pair(f16_t, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
+}
+
 // 16 codes (one 16-byte load) as two 16-byte chunks of 8 operand values.
 template <typename T, typename KV>
 __device__ __forceinline__ void widen16(const u32x4& w, u32x4& lo, u32x4& hi) {
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float f[4];
-    decode4(KV{}, word(w, i), f);
-    packed[2 * i] = Mfma<T>::pack_exact(f[0], f[1]);
-    packed[2 * i + 1] = Mfma<T>::pack_exact(f[2], f[3]);
+    if constexpr (__is_same(KV, KvFp8)) {
+      packed[2 * i] = fp8_pair<false>(T{}, word(w, i));
+      packed[2 * i + 1] = fp8_pair<true>(T{}, word(w, i));
+    } else {
+      float f[4];
+      decode4(KV{}, word(w, i), f);
+      packed[2 * i] = Mfma<T>::pack_exact(f[0], f[1]);
+      packed[2 * i + 1] = Mfma<T>::pack_exact(f[2], f[3]);
+    }
   }
   lo = u32x4{packed[0], packed[1], packed[2], packed[3]};
   hi = u32x4{packed[4], packed[5], packed[6], packed[7]};
@@ -379,12 +397,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       }
     }
 
-    // weights, split into high and low 16-bit parts
+    // weights, split into high and low 16-bit parts.  For 8-bit caches with
+    // bf16 operands the V scale folds into the weights (bf16 keeps float's
+    // exponent range and the split keeps the sign); f16 weights could overflow,
+    // so there the scale multiplies each tile's P.V product instead.
+    constexpr bool kFoldV = kQuant && __is_same(T, bf16_t);
     float pe[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pe[e] = fast_exp2(__builtin_fmaf(x[e], c, -msub));  // x = -inf gives 0
       lsum += pe[e];
+      if constexpr (kFoldV) pe[e] *= vs;
     }
     uint32_t h01, l01, h23, l23;
     Mfma<T>::split2(pe[0], pe[1], h01, l01);
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
       const int chunk = 2 * nb + ((li & 3) >> 1);
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(lds_v3 + swz(tr_row, chunk) + 8 * (li & 1)));
-      if constexpr (kQuant) {
+      if constexpr (kQuant && !kFoldV) {
         f32x4 t = Mfma<T>::k16(phi, vb, f32x4{0.f, 0.f, 0.f, 0.f});
         t = Mfma<T>::k16(plo, vb, t);
 #pragma unroll
