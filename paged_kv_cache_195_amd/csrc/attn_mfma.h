@@ -1,6 +1,6 @@
-// Split-KV paged attention on the matrix cores (gfx950 MFMA), for 16-bit
-// caches when one kv head carries at least 8 query rows (grouped-query decode
-// with G >= 8, or prefill rows).
+// Split-KV paged attention on the matrix cores (gfx950 MFMA), for 16-bit and
+// 8-bit caches: every decode, whatever the group size, and prefill with fewer
+// than 64 query rows per kv head (the shared-tile prefill kernel takes more).
 //
 // A wave owns 16 query rows of one kv head (a row is a (query position, head
 // of the group) pair) and streams its kv head's pages in 16-token tiles:

@@ -1,4 +1,6 @@
-// Split-KV paged attention on the vector ALUs (gfx950, wave64).
+// Split-KV paged attention on the vector ALUs (gfx950, wave64).  The library
+// instantiates it for f32 caches; 16-bit and 8-bit caches run faster on the
+// matrix cores.
 //
 // A workgroup computes, for kpw kv heads of one sequence and one split of its
 // pages, MR query rows per kv head.  A row is a (query position, head of the

@@ -53,9 +53,10 @@ def check_split_partials(w, splits, ws, causal, prefix=None, lens=None):
     assert_close(pl, xl.reshape(rows, splits), w.q.dtype, "part_lse")
 
 
-# (dtype, D, page, Hq, Hkv, Sq, lens, prefix): the three kernels (VALU below 8 rows
-# per kv head, the matrix-core decode kernel from 8, the shared-tile prefill kernel
-# from 64) with offsets before the first key, inside, at L - Sq and past the end.
+# (dtype, D, page, Hq, Hkv, Sq, lens, prefix): the three kernels (the vector-ALU one
+# for f32, the matrix-core decode kernel for 16-bit caches, the shared-tile prefill
+# kernel from 64 rows per kv head) with offsets before the first key, inside, at
+# L - Sq and past the end.
 PREFIX_CASES = [
     ("f32", 64, 16, 4, 2, 3, [37, 200, 90], [-5, 120, 87]),
     ("bf16", 128, 16, 8, 2, 2, [100, 300, 17], [50, -1, 15]),
