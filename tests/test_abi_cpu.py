@@ -99,23 +99,23 @@ def test_workspace_required_for_splits():
 
 def test_split_resolution():
     """Automatic S: at least 256 workgroups (one per compute unit), at most 64
-    and at most one split per 4 table slots (rounded up)."""
+    and at most one split per 8 table slots (rounded up)."""
     # Llama-3-8B decode shape: 256 workgroups of 16 waves (8 kv heads each) fill the GPU
     assert pa.resolve_num_splits(shape(), 0) == 1
     assert pa.workspace_bytes(shape(), 0) == 0
     assert pa.resolve_num_splits(shape(), 5) == 5
     # small batches split so the grid has enough workgroups, capped by the table width
     s3 = shape(batch=8, max_pages_per_seq=63, block_table_stride=63)
-    assert pa.resolve_num_splits(s3, 0) == 16
-    assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=3, block_table_stride=3), 0) == 1
-    assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=5, block_table_stride=5), 0) == 2
+    assert pa.resolve_num_splits(s3, 0) == 8
+    assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=8, block_table_stride=8), 0) == 1
+    assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=9, block_table_stride=9), 0) == 2
     # Qwen3-235B decode shape (G = 16, matrix-core kernel, 4 kv heads per workgroup)
     s5 = shape(num_q_heads=64, num_kv_heads=4, max_pages_per_seq=512, block_table_stride=512,
                num_pages=131072)
     assert pa.resolve_num_splits(s5, 0) == 1
     s1 = shape(dtype=0, batch=2, num_q_heads=4, num_kv_heads=2, head_dim_qk=64, head_dim_v=64,
                max_pages_per_seq=16, block_table_stride=16, num_pages=30)
-    assert pa.resolve_num_splits(s1, 0) == 4
+    assert pa.resolve_num_splits(s1, 0) == 2
     assert pa.resolve_num_splits(shape(batch=0), 0) == PA_EINVAL
     assert pa.resolve_num_splits(shape(), -3) == PA_EINVAL
 
@@ -184,4 +184,4 @@ def test_eight_bit_cache_validation():
     # Llama-3-8B decode shape, 256 workgroups, so no split
     assert pa.resolve_num_splits(shape(kv_dtype=PA_I8), 0) == 1
     assert pa.resolve_num_splits(shape(kv_dtype=PA_FP8_E4M3, batch=8, max_pages_per_seq=63,
-                                       block_table_stride=63), 0) == 16
+                                       block_table_stride=63), 0) == 8
