@@ -1,5 +1,5 @@
 // Template dispatch of the vector-ALU attention kernel over (D, page size,
-// rows per workgroup).  Included once per element type.
+// rows per workgroup).  Included by the f32 instantiation.
 #pragma once
 
 #include "attn_valu.h"

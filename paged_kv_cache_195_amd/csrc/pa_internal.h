@@ -44,12 +44,13 @@ struct AttnPlan {
   int heads_per_wg;  // kv heads per workgroup
 };
 
-// Launch shape compiled for each (element bytes, D, page size, MR).  nl is the
-// number of 16-byte wave loads per page and per cache tensor.  Kernels whose
-// working set fits 128 VGPRs run 16 waves (one 1024-thread workgroup fills a
-// compute unit) and rely on occupancy for loads in flight; larger ones run 8
-// waves.  Measured on the Llama-3-8B decode shape, a deeper per-wave register
-// ring (pages_ahead > 0) gained nothing over occupancy and pushed the larger
+// Launch shape of the vector-ALU kernel for each (element bytes, D, page
+// size, MR).  Kernels whose working set fits 128 VGPRs (at most 4 KiB of K
+// per page and kv head, MR <= 4) run 16 waves (one 1024-thread workgroup
+// fills a compute unit) and rely on occupancy for loads in flight; larger
+// ones run 8 waves.  Measured on the Llama-3-8B decode shape (bf16, when that
+// shape still ran on this kernel), a deeper per-wave register ring
+// (pages_ahead > 0) gained nothing over occupancy and pushed the larger
 // kernels into spills, so every configuration streams one page at a time.
 struct ValuConfig {
   int waves;
