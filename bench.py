@@ -48,12 +48,21 @@ TRAFFIC_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and whitespace runs, so that a change of
+    wording does not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(workload: str) -> str:
-    """sha256 over the sources the workload's kernel is built from."""
+    """sha256 over the code (comments and layout stripped) of the sources the
+    workload's kernel is built from."""
     h = hashlib.sha256()
     for name in sorted(TRAFFIC_SOURCES[workload]):
-        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(KERNEL_SOURCES, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
