@@ -59,12 +59,14 @@ class PaOptions(ctypes.Structure):
 
 
 _lib = None
+_lib_path = None
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libpa.so once and declare the C signatures."""
-    global _lib
-    if _lib is not None:
+    """Load libpa.so once and declare the C signatures.  The library at
+    ``path`` becomes the one every call of this module uses."""
+    global _lib, _lib_path
+    if _lib is not None and _lib_path == path:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(
@@ -90,12 +92,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_resolve_num_splits.restype = ctypes.c_int
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.pa_strerror.restype = ctypes.c_char_p
-    _lib = lib
+    _lib, _lib_path = lib, path
     return lib
 
 
+def _current() -> ctypes.CDLL:
+    """The library calls go to: the last one loaded, else the in-tree build."""
+    return _lib if _lib is not None else load_library()
+
+
 def strerror(status: int) -> str:
-    return load_library().pa_strerror(int(status)).decode()
+    return _current().pa_strerror(int(status)).decode()
 
 
 def _check(status: int, what: str):
@@ -164,7 +171,7 @@ def _scales(name, t, k_cache):
 def _attention(fn_name, q, k_cache, v_cache, block_table, seq_lens, scale, causal, num_splits,
                out, lse, num_pages, workspace, return_workspace, prefix_offset=None,
                page_check=None, k_scale=None, v_scale=None):
-    lib = load_library()
+    lib = _current()
     _validate_tensors(q, k_cache, v_cache, block_table, seq_lens)
     shape = make_shape(q, k_cache, v_cache, block_table, num_pages)
     batch, seq_q, hq, _ = q.shape
@@ -243,7 +250,7 @@ def prefill(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bo
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,
             out=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """LSE merge of ``part_out [rows, S, Dv]`` / ``part_lse [rows, S]`` (float32)."""
-    lib = load_library()
+    lib = _current()
     if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
         raise ValueError("partials must be float32")
     if not (part_out.is_contiguous() and part_lse.is_contiguous() and part_out.is_cuda):
@@ -263,11 +270,11 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,
 
 
 def workspace_bytes(shape: PaShape, num_splits: int = 0) -> int:
-    return int(load_library().pa_workspace_bytes(ctypes.byref(shape), int(num_splits)))
+    return int(_current().pa_workspace_bytes(ctypes.byref(shape), int(num_splits)))
 
 
 def resolve_num_splits(shape: PaShape, num_splits: int = 0) -> int:
-    return int(load_library().pa_resolve_num_splits(ctypes.byref(shape), int(num_splits)))
+    return int(_current().pa_resolve_num_splits(ctypes.byref(shape), int(num_splits)))
 
 
 def split_views(workspace: torch.Tensor, rows: int, num_splits: int, head_dim_v: int):

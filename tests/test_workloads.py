@@ -58,3 +58,41 @@ def test_strided_table_variant():
     storage = w.notes["table_storage"]
     rows = storage[: 8 * 70].view(8, 70)
     assert (rows[:, 63:] == UNMAPPED_PAGE).all()
+
+
+def test_eight_bit_caches():
+    """8-bit generators: code types, scale shape, NaN scales and poison codes in
+    unreferenced pages, poison codes past each sequence's end, never elsewhere."""
+    from paged_kv_cache_195_amd.workloads import POISON_CODE, make_custom
+
+    for kind, dtype in (("int8", torch.int8), ("fp8_e4m3", torch.float8_e4m3fn)):
+        w = make_custom("bf16", [37, 200], 8, 2, 64, 16, seed=3, kv=kind)
+        assert w.kv == kind and w.k_cache.dtype == dtype and w.v_cache.dtype == dtype
+        phys = w.k_cache.shape[0]
+        assert w.k_scale.shape == (phys, 2) and w.k_scale.dtype == torch.float32
+        t = w.table_host
+        used = set(t[0, :3].tolist()) | set(t[1, :13].tolist())
+        unused = sorted(set(range(phys)) - used)
+        assert unused and torch.isnan(w.k_scale[unused]).all() and torch.isnan(w.v_scale[unused]).all()
+        assert torch.isfinite(w.k_scale[sorted(used)]).all()
+        raw = w.k_cache.view(torch.uint8)
+        poison = POISON_CODE[kind]
+        assert (raw[unused] == poison).all()
+        last = int(t[0, 2])                                   # 37 = 2 * 16 + 5 tokens
+        assert (raw[last, 5:] == poison).all() and not (raw[last, :5] == poison).any()
+        assert not (raw[sorted(used - {last, int(t[1, 12])})] == poison).any()
+
+
+def test_missing_library_raises():
+    """The binding never falls back: without the library every call raises."""
+    import pytest
+
+    import paged_kv_cache_195_amd.api as api
+
+    saved = api._lib
+    api._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            api.load_library("/nonexistent/libpa.so")
+    finally:
+        api._lib = saved
