@@ -192,10 +192,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
     for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 32-token half of a tile in two steps: half_scores issues the S
-  // MFMAs, half_finish masks, rescales, forms the weights and runs P . V.
-  // scores of row block rb, row li, tokens tile_tok0 + 32 h + 16 q2 + 4 g + e
+  // A 64-token tile in two 32-token halves.  Scores of row block rb, row li,
+  // tokens tile_tok0 + 32 h + 16 q2 + 4 g + e.
   typedef float Scores[RB][2][4];
+  // the S MFMAs of one half, both row blocks
   auto half_scores = [&](const char* kb, int h, Scores& x) __attribute__((always_inline)) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
@@ -215,51 +215,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         for (int e = 0; e < 4; ++e) x[rb][q2][e] = sacc[rb][e];
     }
   };
-
-  auto half_finish = [&](lds_char* vb3, int h, int tile_tok0, Scores& x) __attribute__((always_inline)) {
-    const int tok0 = tile_tok0 + 32 * h;
-    // mask keys a row may not see, or outside the split (wave-uniform test)
-    if (tok0 + 32 > wave_min_lim || tok0 + 32 > tok_end) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int lim = min(my_lim[rb], tok_end);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[rb][q2][e] = tok0 + 16 * q2 + 4 * g + e < lim ? x[rb][q2][e] : kNegInf;
-      }
-    }
-    // lazy rescale of each row block
+  // keys a row may not see, or outside the split, become -inf (a select, so
+  // stale rows of the LDS tile never reach the arithmetic)
+  auto half_mask = [&](int tok0, Scores& x) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float tmax = kNegInf;
+      const int lim = min(my_lim[rb], tok_end);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = __builtin_fmaxf(tmax, x[rb][q2][e]);
-      const bool raise = tmax * c > ref[rb] + kSlack;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
-        float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
-        rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));
-        const float nref = __builtin_fmaxf(ref[rb], rmax * c);
-        const float nsub = nref == kNegInf ? 0.f : nref;
-        const float alpha = fast_exp2(msub[rb] - nsub);
-        ref[rb] = nref;
-        msub[rb] = nsub;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ae = __builtin_bit_cast(
-              float,
-              __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, alpha)));
-          lsum[rb][e] *= ae;
-#pragma unroll
-          for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb][e] *= ae;
-        }
-      }
+        for (int e = 0; e < 4; ++e)
+          x[rb][q2][e] = tok0 + 16 * q2 + 4 * g + e < lim ? x[rb][q2][e] : kNegInf;
     }
-    // weights as 8 high and 8 low 16-bit values per row block; row sums on
-    // the matrix cores
+  };
+  // weights of one half as 8 high and 8 low 16-bit values per row block, their
+  // row sums on the matrix cores, and O += P . V
+  auto half_pv = [&](lds_char* vb3, int h, Scores& x) __attribute__((always_inline)) {
     u32x4 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -294,20 +265,58 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       }
     }
   };
-  // Both halves' score MFMAs are issued before the first half's softmax, so
-  // the matrix cores compute the second half's scores while the vector ALUs
-  // work on the first (B=1, Sq=L=4096: 466 -> 459 us).  Straight-line tiles
-  // (a masked and an unmasked variant, one rescale decision per tile) let
-  // the compiler interleave further but spill at D = 128 and ran 592 us.
+  // One tile: both halves' score MFMAs; the mask (only on tiles that cross a
+  // row's last key or the split's end); one lazy-rescale decision per row
+  // block for the whole tile (the reference max is raised only when some
+  // score of the tile exceeds it by more than kSlack); then the weights and
+  // P . V of both halves as one straight-line block, so the compiler can
+  // interleave the first half's MFMAs with the second half's exponentials
+  // (iglp_opt(1) steers that interleave).  A wave's last, partial tile
+  // computes its second half too, fully masked: fewer branches beat the
+  // skipped MFMAs (B=1, Sq=L=4096: 455 -> 429 us).  Each wave issues in order,
+  // so without such an interleave the matrix cores and the vector ALUs of a
+  // SIMD were busy together only 8% of the time.
   auto compute_tile = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
     const char* kb = smem + buf * 2 * kBuf;
     lds_char* vb3 = smem3 + buf * 2 * kBuf + kBuf;
-    const bool second = tile_tok0 + 32 < wave_max_lim;  // wave-uniform
     Scores x0, x1;
     half_scores(kb, 0, x0);
-    if (second) half_scores(kb, 1, x1);
-    half_finish(vb3, 0, tile_tok0, x0);
-    if (second) half_finish(vb3, 1, tile_tok0, x1);
+    half_scores(kb, 1, x1);
+    if (tile_tok0 + kTile > wave_min_lim || tile_tok0 + kTile > tok_end) {  // wave-uniform
+      half_mask(tile_tok0, x0);
+      half_mask(tile_tok0 + 32, x1);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(x0[rb][q2][e], x1[rb][q2][e]));
+      const bool raise = tmax * c > ref[rb] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
+        float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
+        rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));
+        const float nref = __builtin_fmaxf(ref[rb], rmax * c);
+        const float nsub = nref == kNegInf ? 0.f : nref;
+        const float alpha = fast_exp2(msub[rb] - nsub);
+        ref[rb] = nref;
+        msub[rb] = nsub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __builtin_bit_cast(
+              float,
+              __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, alpha)));
+          lsum[rb][e] *= ae;
+#pragma unroll
+          for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb][e] *= ae;
+        }
+      }
+    }
+    half_pv(vb3, 0, x0);
+    half_pv(vb3, 1, x1);
+    __builtin_amdgcn_iglp_opt(1);
   };
 
   // ---- tile loop (every wave of the workgroup runs every tile: the LDS
