@@ -57,13 +57,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   const int g = lane >> 4;
   const int li = lane & 15;
 
+  // XCD-aware order.  An MI355X dispatches workgroups round-robin over its 8
+  // XCDs, each with its own L2, and every row group of a (sequence, kv head)
+  // reads the same K/V tiles.  Renumbered so that XCD x runs a contiguous
+  // range of (row group, kv head, sequence), a kv head's tiles stay in one
+  // L2 instead of being fetched by all eight (B=4, Sq=L=1024: 102 -> 78 us;
+  // B=1, Sq=L=4096: 436 -> 376 us).  The renumbering is a bijection for any
+  // grid size; the XCD count only tunes locality.
+  constexpr uint64_t kXcds = 8;
+  const uint64_t gx = gridDim.x, gy = gridDim.y;
+  const uint64_t n_wg = gx * gy * gridDim.z;
+  const uint64_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint64_t xcd = lin % kXcds;
+  const uint64_t per_xcd = n_wg / kXcds, extra = n_wg % kXcds;
+  const uint64_t logical =
+      (xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd) +
+      lin / kXcds;
+  const int bx = static_cast<int>(logical % gx);
+  const int by = static_cast<int>((logical / gx) % gy);
+  const int bz = static_cast<int>(logical / (gx * gy));
   const int S = p.num_splits;
-  const int split = blockIdx.x % S;
+  const int split = bx % S;
   // heaviest (latest) row groups first: they see the most keys
   const int n_rg = gridDim.x / S;
-  const int rg = n_rg - 1 - static_cast<int>(blockIdx.x / S);
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const int rg = n_rg - 1 - bx / S;
+  const int kvh = by;
+  const int b = bz;
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
   const int Sq = p.seq_q;
