@@ -39,7 +39,7 @@ TRAFFIC_FILES = {
 KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
 # the sources each workload's kernel is built from (host planning included)
 _COMMON = ["device_common.h", "page_table.h", "pa_internal.h", "pa_api.cpp"]
-_MFMA = ["attn_mfma.h", "attn_mfma_launch.h", "attn_prefill.h"]
+_MFMA = ["attn_mfma.h", "attn_mfma_launch.h"]   # the decode kernel (prefill shares only the file)
 TRAFFIC_SOURCES = {
     "llama3_8b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
     "qwen3_235b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
