@@ -378,3 +378,32 @@ def test_prefill_kernel_cases(dtype, d, ps, hq, hkv, seq_q, lens, causal, splits
     assert_close(lse, xl, torch.float32, "lse")
     if splits > 1:
         check_partials(w, splits, ws, causal=causal)
+
+
+# (dtype, D, page, Hq, Hkv, Sq, lens, causal): kv-head counts that are not a
+# multiple of 8 (4-wave workgroups, fewer kv heads per workgroup than waves)
+# and group sizes that are not powers of two
+ODD_HEAD_CASES = [
+    ("bf16", 128, 16, 15, 5, 1, [300, 17, 1000], False),   # G = 3, Hkv = 5
+    ("f16", 64, 32, 15, 3, 1, [99, 512], False),           # G = 5, Hkv = 3
+    ("bf16", 128, 16, 12, 6, 1, [257, 31], False),         # G = 2, Hkv = 6
+    ("bf16", 64, 16, 12, 12, 1, [130, 400, 5], False),     # G = 1, Hkv = 12
+    ("bf16", 128, 16, 15, 5, 9, [200, 9], True),           # prefill rows, G = 3
+    ("f16", 128, 32, 14, 2, 20, [150, 20], True),          # G = 7, 140 rows: prefill kernel
+]
+
+
+@pytest.mark.parametrize("case", ODD_HEAD_CASES,
+                         ids=lambda c: f"{c[0]}-D{c[1]}-Hq{c[3]}-Hkv{c[4]}-Sq{c[5]}")
+@pytest.mark.parametrize("splits", [1, 3])
+def test_odd_head_counts(case, splits):
+    dtype, d, ps, hq, hkv, sq, lens, causal = case
+    say(f"odd heads {dtype} D={d} ps={ps} Hq={hq} Hkv={hkv} Sq={sq} lens={lens} S={splits}")
+    w = make_custom(dtype, lens, hq, hkv, d, ps, seq_q=sq, causal=causal, seed=51, device=DEV)
+    out, lse, ws = run(w, splits, return_workspace=True, causal=causal)
+    xo, xl = oracle_full(w, causal=causal)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    assert_close(out, xo, tdt, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+    if splits > 1:
+        check_partials(w, splits, ws, causal=causal)
