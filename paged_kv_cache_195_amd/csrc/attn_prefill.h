@@ -301,7 +301,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
     Scores x0, x1;
     half_scores(kb, 0, x0);
     half_scores(kb, 1, x1);
-    if (tile_tok0 + kTile > wave_min_lim || tile_tok0 + kTile > tok_end) {  // wave-uniform
+    // wave-uniform and rare; the hint keeps the compiler from turning the mask
+    // into selects that every tile would execute (64 vector instructions)
+    if (__builtin_expect(tile_tok0 + kTile > wave_min_lim || tile_tok0 + kTile > tok_end, 0)) {
       half_mask(tile_tok0, x0);
       half_mask(tile_tok0 + 32, x1);
     }
