@@ -18,8 +18,19 @@
 // 32 tokens along K is free as long as both operands agree, so lane l's eight
 // A values are its four weights from each of the two sub-tiles, and its
 // eight B values are the two transposing LDS reads (ds_read_b64_tr_b16) of
-// those sub-tiles -- no data moves between lanes.  P is split into high and
-// low 16-bit parts.  LDS rows use the same XOR swizzle as the decode kernel.
+// those sub-tiles -- no data moves between lanes.  LDS rows use the same XOR
+// swizzle as the decode kernel.
+//
+// P . V runs in f16: each weight is rounded once to f16 (11 significant bits,
+// relative error <= 2^-12; a weight is at most 2^8 under the lazy rescale).
+// f16 caches need nothing more.  For bf16 caches the V tile passes through
+// registers and is converted to f16 on its way into LDS (exact for values of
+// magnitude 2^-14 .. 65504; smaller ones keep an absolute error <= 2^-25).  A
+// V value beyond f16 range becomes infinite and leaves a non-finite
+// accumulator behind, so a workgroup that ends with one recomputes its rows
+// with the bf16 operands: each weight as a high and a low bf16 part (two
+// MFMAs per product, 16 significant bits), V loaded unchanged.  One bf16
+// weight alone (8 bits) is not accurate enough for the bf16 error bound.
 //
 // Causal masking is bottom-right (row i of Sq sits at key position
 // L - Sq + i); tiles past the last key any row of the workgroup can see are
@@ -29,9 +40,24 @@
 // distinct rows, so no cross-wave merge is needed.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_mfma.h"
 
 namespace pa {
+
+// Two floats as a packed f16 pair, each rounded to nearest even (one
+// v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// A packed bf16 pair as a packed f16 pair: exact for magnitudes 2^-14 ..
+// 65504, rounded to nearest even below, infinite above.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return f32x2_to_f16x2(__builtin_bit_cast(float, w << 16),
+                        __builtin_bit_cast(float, w & 0xffff0000u));
+}
 
 template <typename T, int D, int PS, int NW, int RB>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const AttnParams p) {
@@ -51,6 +77,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   constexpr int kRowsPerWaveQ = 16 * RB;         // query rows per wave
   constexpr int kBuf = kTile * kRowBytes;        // one K or V tile in LDS
   constexpr float kSlack = 8.f;
+  constexpr bool kConvertV = std::is_same<T, bf16_t>::value;  // bf16 V goes to f16
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,7 +188,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
 
   // Issue this wave's loads of a tile; returns true when some of its rows lie
   // at or past tok_end (their V rows must then be zeroed once the loads land).
-  auto load_tile = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
+  // With kViaRegs the V chunks go to vr instead of LDS (store_v converts and
+  // stores them).
+  typedef u32x4 VRegs[kLoads];
+  auto load_tile = [&](auto via_regs, int buf, int tile_tok0, VRegs& vr)
+                       __attribute__((always_inline)) {
+    constexpr bool kViaRegs = decltype(via_regs)::value;
     const int row0 = kRowsPerWave * wave;                    // first tile row of this wave
     const int tok = tile_tok0 + row0;
     if (tok < tok_end) {                                     // wave-uniform
@@ -176,11 +208,43 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         const int lds_off = buf * 2 * kBuf + (row0 + j * kRowsPerLoad) * kRowBytes;
         __builtin_amdgcn_global_load_lds((global_ptr)(kbase + base + off),
                                          (lds_ptr)(smem3 + lds_off), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((global_ptr)(vbase + base + off),
-                                         (lds_ptr)(smem3 + lds_off + kBuf), 16, 0, 0);
+        if constexpr (kViaRegs)
+          vr[j] = *reinterpret_cast<const u32x4*>(vbase + base + off);
+        else
+          __builtin_amdgcn_global_load_lds((global_ptr)(vbase + base + off),
+                                           (lds_ptr)(smem3 + lds_off + kBuf), 16, 0, 0);
       }
+    } else if constexpr (kViaRegs) {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) vr[j] = u32x4{0u, 0u, 0u, 0u};
     }
     return tok + kRowsPerWave > tok_end;
+  };
+  // The V chunks of load_tile's register path, as f16, where the direct load
+  // would have put them (lane l's 16 bytes at l * 16 of each wave load); rows
+  // at or past tok_end are stored as zeros.
+  auto store_v = [&](int buf, int tile_tok0, const VRegs& vr) __attribute__((always_inline)) {
+    char* vb = smem + buf * 2 * kBuf + kBuf;
+    if (__builtin_expect(tile_tok0 + kRowsPerWave * (wave + 1) <= tok_end, 1)) {  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        u32x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = bf16x2_to_f16x2(vr[j][i]);
+        *reinterpret_cast<u32x4*>(vb + (kRowsPerWave * wave + j * kRowsPerLoad) * kRowBytes +
+                                  16 * lane) = h;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int r0 = kRowsPerWave * wave + j * kRowsPerLoad;
+        const bool keep = tile_tok0 + r0 + lr < tok_end;
+        u32x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = keep ? bf16x2_to_f16x2(vr[j][i]) : 0u;
+        *reinterpret_cast<u32x4*>(vb + r0 * kRowBytes + 16 * lane) = h;
+      }
+    }
   };
   // Zero this wave's V rows at or past tok_end (past the sequence end, in a
   // page of the next split, or never loaded), after its loads have landed, so
@@ -201,18 +265,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   // four token groups are added at the end).  Summing on the vector ALUs
   // instead of with MFMAs against a block of ones saves 8 of 104 MFMAs per
   // tile (B=1, Sq=L=4096: 381 -> 371 us); it normalises by the float weights,
-  // within 2^-16 of the high + low parts the P . V MFMAs use.
+  // within 2^-12 of the rounded weights the P . V MFMAs use.
   float ref[RB], msub[RB];
   f32x4 o[RB][kNBlocks];
   float lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    ref[rb] = kNegInf;
-    msub[rb] = 0.f;
-    lsum[rb] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
 
   // A 64-token tile in two 32-token halves.  Scores of row block rb, row li,
   // tokens tile_tok0 + 32 h + 16 q2 + 4 g + e.
@@ -250,9 +306,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
           x[rb][q2][e] = tok0 + 16 * q2 + 4 * g + e < lim ? x[rb][q2][e] : kNegInf;
     }
   };
-  // weights of one half as 8 high and 8 low 16-bit values per row block, their
-  // row sums, and O += P . V
-  auto half_pv = [&](lds_char* vb3, int h, Scores& x) __attribute__((always_inline)) {
+  // weights of one half, 8 per row block (as f16, or as high and low bf16
+  // parts), their row sums, and O += P . V
+  auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x) __attribute__((always_inline)) {
+    constexpr bool kF16 = decltype(f16pv)::value;
     u32x4 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -264,7 +321,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
           pe[4 * q2 + e] = fast_exp2(__builtin_fmaf(x[rb][q2][e], c, -msub[rb]));
       uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) Mfma<T>::split2(pe[2 * w], pe[2 * w + 1], hi[w], lo[w]);
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (kF16) {
+          hi[w] = f32x2_to_f16x2(pe[2 * w], pe[2 * w + 1]);
+          lo[w] = 0u;
+        } else {
+          Mfma<T>::split2(pe[2 * w], pe[2 * w + 1], hi[w], lo[w]);
+        }
+      }
       phi[rb] = u32x4{hi[0], hi[1], hi[2], hi[3]};
       plo[rb] = u32x4{lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
@@ -282,8 +346,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
           __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        o[rb][nb] = Mfma<T>::k32(phi[rb], vv, o[rb][nb]);
-        o[rb][nb] = Mfma<T>::k32(plo[rb], vv, o[rb][nb]);
+        if constexpr (kF16) {
+          o[rb][nb] = Mfma<f16_t>::k32(phi[rb], vv, o[rb][nb]);
+        } else {
+          o[rb][nb] = Mfma<T>::k32(phi[rb], vv, o[rb][nb]);
+          o[rb][nb] = Mfma<T>::k32(plo[rb], vv, o[rb][nb]);
+        }
       }
     }
   };
@@ -298,7 +366,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   // skipped MFMAs (B=1, Sq=L=4096: 455 -> 429 us).  Each wave issues in order,
   // so without such an interleave the matrix cores and the vector ALUs of a
   // SIMD were busy together only 8% of the time.
-  auto compute_tile = [&](int buf, int tile_tok0) __attribute__((always_inline)) {
+  auto compute_tile = [&](auto f16pv, int buf, int tile_tok0) __attribute__((always_inline)) {
     const char* kb = smem + buf * 2 * kBuf;
     lds_char* vb3 = smem3 + buf * 2 * kBuf + kBuf;
     Scores x0, x1;
@@ -338,26 +406,72 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         }
       }
     }
-    half_pv(vb3, 0, x0);
-    half_pv(vb3, 1, x1);
+    half_pv(f16pv, vb3, 0, x0);
+    half_pv(f16pv, vb3, 1, x1);
     __builtin_amdgcn_iglp_opt(1);
   };
 
   // ---- tile loop (every wave of the workgroup runs every tile: the LDS
-  // buffers are shared, so the barriers must be reached by all of them)
+  // buffers are shared, so the barriers must be reached by all of them).
+  // f16pv: P . V in f16 (V converted on the way in for bf16 caches), else
+  // with high and low bf16 weights.
   const int n_tiles = tok_end > tok_begin ? (tok_end - tok_begin + kTile - 1) / kTile : 0;
-  if (n_tiles > 0) {
-    if (load_tile(0, tok_begin)) zero_tail(0, tok_begin);
-  }
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int tok0 = tok_begin + t * kTile;
-    const bool more = t + 1 < n_tiles;
-    const bool tail = more && load_tile((t + 1) & 1, tok0 + kTile);
-    // a wave whose rows see none of this tile skips the arithmetic
-    if (tok0 < wave_max_lim) compute_tile(t & 1, tok0);
-    if (tail) zero_tail((t + 1) & 1, tok0 + kTile);
-    __syncthreads();  // the next tile has landed (the compiler waits for it) and this one is done
+  auto run = [&](auto f16pv) __attribute__((always_inline)) {
+    constexpr bool kViaRegs = decltype(f16pv)::value && kConvertV;
+    const std::integral_constant<bool, kViaRegs> via_regs;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ref[rb] = kNegInf;
+      msub[rb] = 0.f;
+      lsum[rb] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    VRegs vr;
+    if (n_tiles > 0) {
+      const bool tail = load_tile(via_regs, 0, tok_begin, vr);
+      if constexpr (kViaRegs)
+        store_v(0, tok_begin, vr);
+      else if (tail)
+        zero_tail(0, tok_begin);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int tok0 = tok_begin + t * kTile;
+      const bool more = t + 1 < n_tiles;
+      const bool tail = more && load_tile(via_regs, (t + 1) & 1, tok0 + kTile, vr);
+      // a wave whose rows see none of this tile skips the arithmetic
+      if (tok0 < wave_max_lim) compute_tile(f16pv, t & 1, tok0);
+      if constexpr (kViaRegs) {
+        if (more) store_v((t + 1) & 1, tok0 + kTile, vr);
+      } else if (tail) {
+        zero_tail((t + 1) & 1, tok0 + kTile);
+      }
+      __syncthreads();  // the next tile has landed (the compiler waits for it) and this one is done
+    }
+  };
+  run(std::true_type());
+  if constexpr (kConvertV) {
+    // a V value beyond f16 range (or a non-finite input) left a non-finite
+    // accumulator: 0 * inf and 0 * NaN are NaN
+    float z = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < kNBlocks; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z = __builtin_fmaf(o[rb][nb][e], 0.f, z);
+    int* flags = reinterpret_cast<int*>(smem);  // the tile buffers are free after the last barrier
+    const bool bad = __builtin_amdgcn_ballot_w64(z != z) != 0;  // all lanes take part
+    if (lane == 0) flags[wave] = bad;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= flags[w];
+    if (redo) {  // workgroup-uniform, rare
+      __syncthreads();  // every wave has read the flags before the loads reuse the buffers
+      run(std::false_type());
+    }
   }
 
   // ---- finish: normalize and write; row 4 g + e of the O layout takes its

@@ -380,6 +380,35 @@ def test_prefill_kernel_cases(dtype, d, ps, hq, hkv, seq_q, lens, causal, splits
         check_partials(w, splits, ws, causal=causal)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_bf16_v_beyond_f16_range(splits):
+    """The prefill kernel multiplies P . V in f16 and converts bf16 V tiles on
+    the way in; V values beyond f16 range (65504) send a workgroup back over
+    its rows with bf16 operands.  Huge values sit in a token every row of the
+    last row group sees, in one only the last rows see (the others multiply it
+    by a zero weight), and tiny values (f16 subnormal range) elsewhere."""
+    lens = [300, 150, 64]
+    say(f"prefill bf16 with V beyond f16 range, lens={lens} S={splits}")
+    w = make_custom("bf16", lens, 32, 8, 128, 16, seq_q=64, causal=True, seed=22, device=DEV)
+    table = w.table_host
+    def put(b, tok, kvh, dims, value):
+        page, slot = int(table[b, tok // 16]), tok % 16
+        w.v_cache[page, slot, kvh, dims] = value
+    put(0, 10, 3, slice(0, 128, 5), 1.0e5)
+    put(0, 290, 3, slice(7, 9), -3.0e9)
+    put(1, 100, 0, slice(0, 64), 7.0e4)
+    put(2, 5, 5, slice(0, 128), 3.0e-7)
+    put(2, 40, 6, slice(0, 128, 3), -2.0e-6)
+    torch.cuda.synchronize()
+    out, lse, ws = run(w, splits, return_workspace=True, causal=True)
+    xo, xl = oracle_full(w, causal=True)
+    assert np.abs(xo).max() > 1e4
+    assert_close(out, xo, torch.bfloat16, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+    if splits > 1:
+        check_partials(w, splits, ws, causal=True)
+
+
 # (dtype, D, page, Hq, Hkv, Sq, lens, causal): kv-head counts that are not a
 # multiple of 8 (4-wave workgroups, fewer kv heads per workgroup than waves)
 # and group sizes that are not powers of two
