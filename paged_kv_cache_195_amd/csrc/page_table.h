@@ -29,9 +29,13 @@ struct PageTable {
   int n_pages;          // ceil(seq_len / page_size): slots that may be read
 
   // Physical page id in slot `slot`, wave-uniform.  The caller guarantees
-  // 0 <= slot < n_pages; `slot` is wave-uniform.
+  // 0 <= slot < n_pages; `slot` is wave-uniform.  The read goes through the
+  // constant address space (the table does not change while a kernel runs),
+  // which makes it a scalar load even in kernels whose LDS-DMA copies keep
+  // the compiler from proving that on its own.
   __device__ __forceinline__ uint32_t id(int slot) const {
-    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(row[slot]));
+    typedef __attribute__((address_space(4))) const int32_t* const_ptr;
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(((const_ptr)row)[slot]));
   }
   // Byte offset of page `page_id` from the start of the cache.
   __device__ __forceinline__ int64_t base_of(uint32_t page_id) const {

@@ -409,6 +409,39 @@ def test_prefill_bf16_v_beyond_f16_range(splits):
         check_partials(w, splits, ws, causal=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("first", [True, False])
+def test_prefill_weights_in_f16_subnormal_range(dtype, first):
+    """One dominant key and 2000 keys each weighted e^-10.4 (about 3e-5 of it,
+    below the smallest normal f16, 2^-14): the small weights carry ~6% of the
+    mass.  V is 0 for the dominant key and 1 elsewhere, so the output is that
+    mass share.  With the dominant key first the small weights are formed
+    relative to it (f16 subnormals in P . V); last, they are formed relative to
+    each other and rescaled when it arrives."""
+    lens = [2048, 2001]
+    say(f"prefill {dtype} weights in the f16 subnormal range, dominant key first={first}")
+    w = make_custom(dtype, lens, 32, 8, 128, 16, seq_q=16, seed=23, device=DEV)
+    w.q.zero_()
+    w.q[..., 0] = 1.0
+    for b, length in enumerate(lens):
+        dom = 0 if first else length - 1
+        t = torch.arange(length)
+        pages = w.table_host[b, t // 16].long().to(DEV)
+        slots = (t % 16).to(DEV)
+        w.k_cache[pages, slots] = 0.0
+        w.v_cache[pages, slots] = 1.0
+        page, slot = int(w.table_host[b, dom // 16]), dom % 16
+        w.k_cache[page, slot, :, 0] = 118.0
+        w.v_cache[page, slot, :, :] = 0.0
+    torch.cuda.synchronize()
+    out, lse = run(w, 1, causal=False)
+    xo, xl = oracle_full(w, causal=False)
+    assert 0.04 < xo.min() and xo.max() < 0.07
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    assert_close(out, xo, tdt, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+
+
 # (dtype, D, page, Hq, Hkv, Sq, lens, causal): kv-head counts that are not a
 # multiple of 8 (4-wave workgroups, fewer kv heads per workgroup than waves)
 # and group sizes that are not powers of two
