@@ -214,9 +214,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
           __builtin_amdgcn_global_load_lds((global_ptr)(vbase + base + off),
                                            (lds_ptr)(smem3 + lds_off + kBuf), 16, 0, 0);
       }
-    } else if constexpr (kViaRegs) {
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) vr[j] = u32x4{0u, 0u, 0u, 0u};
     }
     return tok + kRowsPerWave > tok_end;
   };
@@ -234,6 +231,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         *reinterpret_cast<u32x4*>(vb + (kRowsPerWave * wave + j * kRowsPerLoad) * kRowBytes +
                                   16 * lane) = h;
       }
+    } else if (tile_tok0 + kRowsPerWave * wave >= tok_end) {  // nothing was loaded
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j)
+        *reinterpret_cast<u32x4*>(vb + (kRowsPerWave * wave + j * kRowsPerLoad) * kRowBytes +
+                                  16 * lane) = u32x4{0u, 0u, 0u, 0u};
     } else {
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
           x[rb][q2][e] = tok0 + 16 * q2 + 4 * g + e < lim ? x[rb][q2][e] : kNegInf;
     }
   };
-  // weights of one half, 8 per row block (as f16, or as high and low bf16
-  // parts), their row sums, and O += P . V
+  // weights 2^x of one half's exponents, 8 per row block (as f16, or as high
+  // and low bf16 parts), their row sums, and O += P . V
   auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x) __attribute__((always_inline)) {
     constexpr bool kF16 = decltype(f16pv)::value;
     u32x4 phi[RB], plo[RB];
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pe[4 * q2 + e] = fast_exp2(__builtin_fmaf(x[rb][q2][e], c, -msub[rb]));
+          pe[4 * q2 + e] = fast_exp2(x[rb][q2][e]);  // x holds the exponent
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -378,24 +380,45 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       half_mask(tile_tok0, x0);
       half_mask(tile_tok0 + 32, x1);
     }
+    // scores become exponents y = x c - msub in place (an FMA's result is a
+    // canonical float, so the max below needs no quieting of its inputs and
+    // runs as v_max3); the tile raises the reference when some y exceeds
+    // kSlack, or when the reference is still -inf and some key is visible
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float tmax = kNegInf;
+      float yv[16];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(x0[rb][q2][e], x1[rb][q2][e]));
-      const bool raise = tmax * c > ref[rb] + kSlack;
+        for (int e = 0; e < 4; ++e) {
+          x0[rb][q2][e] = __builtin_fmaf(x0[rb][q2][e], c, -msub[rb]);
+          x1[rb][q2][e] = __builtin_fmaf(x1[rb][q2][e], c, -msub[rb]);
+          yv[4 * q2 + e] = x0[rb][q2][e];
+          yv[8 + 4 * q2 + e] = x1[rb][q2][e];
+        }
+      float tmax = __builtin_fmaxf(__builtin_fmaxf(yv[0], yv[1]), yv[2]);
+#pragma unroll
+      for (int k = 3; k + 1 < 16; k += 2)
+        tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, yv[k]), yv[k + 1]);
+      tmax = __builtin_fmaxf(tmax, yv[15]);
+      const bool raise = tmax > (ref[rb] == kNegInf ? kNegInf : kSlack);
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
         float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
         rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));
-        const float nref = __builtin_fmaxf(ref[rb], rmax * c);
+        const float nref = __builtin_fmaxf(ref[rb], rmax + msub[rb]);
         const float nsub = nref == kNegInf ? 0.f : nref;
-        const float alpha = fast_exp2(msub[rb] - nsub);
+        const float shift = msub[rb] - nsub;
+        const float alpha = fast_exp2(shift);
         ref[rb] = nref;
         msub[rb] = nsub;
         lsum[rb] *= alpha;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[rb][q2][e] += shift;
+            x1[rb][q2][e] += shift;
+          }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float ae = __builtin_bit_cast(
