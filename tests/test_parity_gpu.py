@@ -136,6 +136,19 @@ def test_deterministic_reruns():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_deterministic_reruns(dtype):
+    """The prefill kernel (shared tiles, f16 P . V, split partials) gives the
+    same bits on every run."""
+    say(f"prefill rerun determinism {dtype}")
+    w = make_custom(dtype, [700, 333, 1024], 32, 8, 128, 16, seq_q=64, causal=True, seed=24,
+                    device=DEV)
+    for splits in (1, 3):
+        a = run(w, splits, causal=True)
+        b = run(w, splits, causal=True)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 def test_q_zero_closed_form():
     """q = 0: lse = ln(L) and out = mean of the valid V rows, for every split count."""
     say("q=0 closed form tiny_f32")
@@ -380,25 +393,26 @@ def test_prefill_kernel_cases(dtype, d, ps, hq, hkv, seq_q, lens, causal, splits
         check_partials(w, splits, ws, causal=causal)
 
 
+@pytest.mark.parametrize("d,ps", [(128, 16), (64, 32)])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_prefill_bf16_v_beyond_f16_range(splits):
+def test_prefill_bf16_v_beyond_f16_range(d, ps, splits):
     """The prefill kernel multiplies P . V in f16 and converts bf16 V tiles on
     the way in; V values beyond f16 range (65504) send a workgroup back over
     its rows with bf16 operands.  Huge values sit in a token every row of the
     last row group sees, in one only the last rows see (the others multiply it
     by a zero weight), and tiny values (f16 subnormal range) elsewhere."""
     lens = [300, 150, 64]
-    say(f"prefill bf16 with V beyond f16 range, lens={lens} S={splits}")
-    w = make_custom("bf16", lens, 32, 8, 128, 16, seq_q=64, causal=True, seed=22, device=DEV)
+    say(f"prefill bf16 with V beyond f16 range, D={d} page {ps} lens={lens} S={splits}")
+    w = make_custom("bf16", lens, 32, 8, d, ps, seq_q=64, causal=True, seed=22, device=DEV)
     table = w.table_host
     def put(b, tok, kvh, dims, value):
-        page, slot = int(table[b, tok // 16]), tok % 16
+        page, slot = int(table[b, tok // ps]), tok % ps
         w.v_cache[page, slot, kvh, dims] = value
-    put(0, 10, 3, slice(0, 128, 5), 1.0e5)
+    put(0, 10, 3, slice(0, d, 5), 1.0e5)
     put(0, 290, 3, slice(7, 9), -3.0e9)
-    put(1, 100, 0, slice(0, 64), 7.0e4)
-    put(2, 5, 5, slice(0, 128), 3.0e-7)
-    put(2, 40, 6, slice(0, 128, 3), -2.0e-6)
+    put(1, 100, 0, slice(0, d // 2), 7.0e4)
+    put(2, 5, 5, slice(0, d), 3.0e-7)
+    put(2, 40, 6, slice(0, d, 3), -2.0e-6)
     torch.cuda.synchronize()
     out, lse, ws = run(w, splits, return_workspace=True, causal=True)
     xo, xl = oracle_full(w, causal=True)
