@@ -5,11 +5,11 @@
 // A workgroup owns 16 * RB * NW rows of one kv head; wave w owns RB blocks of
 // 16 rows.  The workgroup walks its split's keys in 64-token tiles.  Each
 // tile of K and V is loaded once, cooperatively (every wave loads whole rows
-// of it with global_load_lds_dwordx4, straight into LDS, no registers), into
-// one of two LDS buffers, and every wave computes its rows against it, so
-// each K/V byte read from memory serves 16 * RB * NW rows and each operand
-// read from LDS serves RB row blocks.  The next tile's loads are issued
-// before the current tile is computed.
+// of it; K, and V of f16 caches, with global_load_lds_dwordx4 straight into
+// LDS), into one of two LDS buffers, and every wave computes its rows against
+// it, so each K/V byte read from memory serves 16 * RB * NW rows and each
+// operand read from LDS serves RB row blocks.  The next tile's loads are
+// issued before the current tile is computed.
 //
 // Per 16-token sub-tile and row block, S^T = K . Q^T is the decode MFMA
 // kernel's product (v_mfma_f32_16x16x32, K from LDS, Q^T in registers); its
