@@ -179,3 +179,27 @@ def test_page_check_lengths_and_prefill():
         assert_close(lse, xl, torch.float32, "lse")
         if splits > 1:
             check_split_partials(w, splits, ws, False, prefix, lens=att)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_variable_length_queries_by_padding(dtype):
+    """Sequences with their own query counts, padded to one Sq: with
+    prefix_offset[b] = L_b - q_b the first q_b rows of sequence b equal a causal
+    prefill of just those q_b queries (the padding rows are computed and
+    ignored)."""
+    lens = [300, 64, 150, 1000]
+    qlens = [5, 64, 20, 37]
+    sq = 64
+    say(f"variable-length queries by padding, {dtype}, lens={lens} q={qlens}")
+    w = make_custom(dtype, lens, 32, 8, 128, 16, seq_q=sq, seed=37, device=DEV)
+    prefix = [x - q for x, q in zip(lens, qlens)]
+    k, v = host_caches(w)
+    qh = host(w.q)
+    table = w.table_host.numpy()
+    for splits in (1, 3):
+        out, lse, _ = call(w, False, splits, prefix=prefix, decode=False)
+        for b, (length, q) in enumerate(zip(lens, qlens)):
+            xo, xl = O.attention(qh[b:b + 1, :q], k, v, table[b:b + 1], np.array([length]),
+                                 w.scale, True)
+            assert_close(out[b:b + 1, :q], xo, TDT[dtype], f"out b={b}")
+            assert_close(lse[b:b + 1, :q], xl, torch.float32, f"lse b={b}")
