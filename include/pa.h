@@ -107,6 +107,16 @@ typedef struct pa_shape {
  *   any group size Hq / Hkv >= 1; B <= 65535 and Hkv <= 65535.
  *   8-bit caches (kv_dtype PA_I8 or PA_FP8_E4M3): dtype F16 or BF16 and
  *   D == Dv in {64, 128}.
+ *
+ * Accuracy: against exact attention (8-bit codes times their scales taken as
+ * the exact cache values), each output element is within 2e-3 + 2^-8 |x| for
+ * F16/BF16 (the bound of rocm-libraries "one K/V resource per page on the
+ * gfx942 2D i64 path", Coverage) and 1e-5 + 1e-5 |x| for F32; the float32
+ * LSE and split partials within 1e-5 + 1e-5 |x| (partials of 16-bit problems
+ * within the 16-bit bound).  Scores and the softmax run in float32; 16-bit
+ * problems multiply on the matrix cores with the softmax weights kept to at
+ * least 11 significant bits.  Results are deterministic: the same inputs give
+ * the same bits on every call.
  */
 
 /*
