@@ -120,6 +120,29 @@ def test_split_resolution():
     assert pa.resolve_num_splits(shape(), -3) == PA_EINVAL
 
 
+def test_split_resolution_prefill():
+    """Automatic S for prefill shapes: the shared-tile kernel's 128-row
+    workgroups already fill the GPU at the benchmark shapes; small ones split."""
+    # B=4, Sq=L=1024, GQA 32/8: 32 row groups x 8 kv heads x 4 sequences = 1024 workgroups
+    s = shape(batch=4, seq_q=1024, max_pages_per_seq=64, block_table_stride=64, num_pages=256)
+    assert pa.resolve_num_splits(s, 0) == 1 and pa.workspace_bytes(s, 0) == 0
+    # B=1, Sq=L=4096, GQA 64/8: 256 row groups x 8 kv heads = 2048 workgroups
+    s = shape(batch=1, seq_q=4096, num_q_heads=64, max_pages_per_seq=256, block_table_stride=256,
+              num_pages=256)
+    assert pa.resolve_num_splits(s, 0) == 1
+    # B=1, Sq=64, GQA 32/8: 2 row groups x 8 kv heads = 16 workgroups; 16 splits would
+    # fill the GPU but the 64-slot table caps S at 8
+    s = shape(batch=1, seq_q=64, max_pages_per_seq=64, block_table_stride=64, num_pages=64)
+    assert pa.resolve_num_splits(s, 0) == 8
+    rows = 64 * 32
+    assert pa.workspace_bytes(s, 0) == rows * 8 * 128 * 4 + rows * 8 * 4
+    # f16, D=32, one head, Sq=1024 (the 16-row matrix-core kernel): 64 workgroups, S=4
+    s = shape(dtype=1, batch=1, seq_q=1024, num_q_heads=1, num_kv_heads=1, head_dim_qk=32,
+              head_dim_v=32, page_size=32, max_pages_per_seq=32, block_table_stride=32,
+              num_pages=32)
+    assert pa.resolve_num_splits(s, 0) == 4
+
+
 def test_combine_validation():
     lib = pa.load_library()
     assert lib.pa_combine(9, 4, 2, 128, FAKE, FAKE, FAKE, None, None) == PA_EINVAL
