@@ -149,6 +149,19 @@ def test_prefill_deterministic_reruns(dtype):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("lens", [[4096], [1000, 3000]])
+def test_small_batch_decode_auto_plan(lens):
+    """One or two sequences: the automatic plan splits each sequence 32 ways
+    and gives each workgroup one kv head (8 waves on its pages, merged in
+    LDS) so the grid still fills the GPU."""
+    say(f"small-batch decode, automatic plan, lens={lens}")
+    w = make_custom("bf16", lens, 32, 8, 128, 16, seed=25, device=DEV)
+    out, lse = run(w, 0)
+    xo, xl = oracle_full(w)
+    assert_close(out, xo, torch.bfloat16, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+
+
 def test_q_zero_closed_form():
     """q = 0: lse = ln(L) and out = mean of the valid V rows, for every split count."""
     say("q=0 closed form tiny_f32")
