@@ -4,6 +4,7 @@
 
 #include "attn_mfma.h"
 #include "attn_prefill.h"
+#include "attn_prefill_pp.h"
 
 namespace pa {
 
@@ -41,12 +42,18 @@ hipError_t launch_attn_mfma_dp(const AttnParams& p, const AttnPlan& plan, int ba
 template <typename T, int D, int PS>
 hipError_t launch_attn_prefill_dp(const AttnParams& p, const AttnPlan& plan, int batch,
                                   hipStream_t stream) {
-  if (plan.waves != kPrefillWaves || plan.rows_per_wg != 16 * kPrefillRowBlocks * kPrefillWaves ||
+  constexpr int kWaves = prefill_waves(D);
+  if (plan.waves != kWaves || plan.rows_per_wg != 16 * kPrefillRowBlocks * kWaves ||
       plan.heads_per_wg != 1)
     return hipErrorInvalidValue;
   const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads, batch);
-  attn_prefill_kernel<T, D, PS, kPrefillWaves, kPrefillRowBlocks>
-      <<<grid, dim3(kPrefillWaves * 64), 0, stream>>>(p);
+  if constexpr (kWaves == kPrefillTeamWaves) {
+    static_assert(kPrefillRowBlocks == 2, "the two-team kernel holds two row blocks per wave");
+    attn_prefill_pp_kernel<T, D, PS><<<grid, dim3(kWaves * 64), 0, stream>>>(p);
+  } else {
+    attn_prefill_kernel<T, D, PS, kWaves, kPrefillRowBlocks>
+        <<<grid, dim3(kWaves * 64), 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

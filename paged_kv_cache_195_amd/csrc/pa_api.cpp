@@ -86,8 +86,8 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   plan.prefill = !quant && plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
-    plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * pa::kPrefillWaves;
-    plan.waves = pa::kPrefillWaves;
+    plan.waves = pa::prefill_waves(s->head_dim_qk);
+    plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * plan.waves;
   } else if (plan.mfma) {
     plan.rows_per_wg = 16;
     plan.waves = (!quant && s->num_kv_heads % 8 != 0) ? pa::kMfmaWavesNarrow : pa::kMfmaWaves;

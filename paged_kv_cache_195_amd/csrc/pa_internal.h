@@ -81,10 +81,15 @@ constexpr int kMfmaWavesNarrow = 4;
 // LDS a 4-wave workgroup holds (static plus reserved): more than a third of a
 // compute unit's 160 KiB, so at most two are resident.
 constexpr int kMfmaLdsPerNarrowWg = 56 * 1024;
-// The shared-tile prefill kernel: kPrefillRowBlocks blocks of 16 rows per
-// wave, kPrefillWaves waves, one kv head per workgroup; D in {64, 128}.
+// The shared-tile prefill kernels: kPrefillRowBlocks blocks of 16 rows per
+// wave, one kv head per workgroup; D = 64 takes the single-team kernel with
+// kPrefillWaves waves, D = 128 the two-team kernel with kPrefillTeamWaves.
 constexpr int kPrefillWaves = 4;
+constexpr int kPrefillTeamWaves = 8;
 constexpr int kPrefillRowBlocks = 2;
+constexpr int prefill_waves(int head_dim) {
+  return head_dim == 128 ? kPrefillTeamWaves : kPrefillWaves;
+}
 constexpr int kPrefillMinRows = 64;
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFp8E4M3 = 4 };
