@@ -28,7 +28,8 @@
 // K . Q^T with v_mfma_f32_16x16x32 (K from LDS, Q^T in registers), the mask
 // only on tiles that cross a row's last key or the split's end, one
 // lazy-rescale decision per row block per tile (exponents y = x c - msub; the
-// reference max rises only when some y exceeds the slack), weights rounded
+// reference max rises only when some y exceeds the slack, which the main
+// loop detects on the sum of a lane's weights), weights rounded
 // once to f16, P . V on the f16 matrix cores with the transposing LDS read
 // (bf16 V converted to f16 on its way into LDS).  A bf16 V value beyond f16
 // range leaves a non-finite accumulator; a workgroup that ends with one
@@ -274,10 +275,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
           for (int e = 0; e < 4; ++e) x[h][rb][q2][e] = sacc[rb][e];
       }
   };
-  // Scores to exponents y = x c - msub in place: the mask (only on tiles that
-  // cross a row's last key or the split's end), then one lazy-rescale
-  // decision per row block for the tile (an FMA's result is a canonical
-  // float, so the maximum runs as v_max3 with no quieting of its inputs).
+  // Scores to exponents y = x c - msub in place (the recompute path): the
+  // mask (only on tiles that cross a row's last key or the split's end), then
+  // one lazy-rescale decision per row block for the tile (an FMA's result is
+  // a canonical float, so the maximum runs as v_max3 with no quieting of its
+  // inputs).
   auto exponents = [&](int tile_tok0, Scores& x) __attribute__((always_inline)) {
     if (__builtin_expect(tile_tok0 + kTile > wave_min_lim || tile_tok0 + kTile > tok_end, 0)) {
 #pragma unroll
@@ -335,25 +337,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
       }
     }
   };
-  // Weights 2^y of one half as packed f16 (one rounding each), and their
-  // float row sums.
   typedef u32x4 Weights[2][RB];
-  auto weights_f16 = [&](const Scores& x, Weights& pw) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float pe[8];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pe[4 * q2 + e] = fast_exp2(x[h][rb][q2][e]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pw[h][rb][w] = f32x2_to_f16x2(pe[2 * w], pe[2 * w + 1]);
-#pragma unroll
-        for (int w = 0; w < 8; ++w) lsum[rb] += pe[w];
-      }
-  };
   // O += P . V for one 32-token half (lane l's eight A values are its weights
   // of the half's two 16-token sub-tiles; its eight B values the two
   // transposing LDS reads of those sub-tiles).  kHiLo: weights as high and
@@ -381,6 +365,83 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
           o[rb][nb] = Mfma<f16_t>::k32(phi[rb], vv, o[rb][nb]);
         }
       }
+    }
+  };
+  // The main loop's softmax of one tile: exponents, weights 2^y as packed
+  // f16, row sums.  The lazy rescale needs to know whether some y exceeds
+  // the slack (a weight above 2^kSlack); a lane's weights can only hold one
+  // if their sum does, so the tile is checked on that sum, which the row sum
+  // needs anyway, instead of on a maximum taken before the exponentials.  A
+  // lane over the limit, or a row with no reference yet, sends the wave to
+  // the exact test: the maximum, the raise of exponents() above, and the
+  // weights again.
+  auto softmax_f16 = [&](int tile_tok0, Scores& xs, Weights& pw) __attribute__((always_inline)) {
+    if (__builtin_expect(tile_tok0 + kTile > wave_min_lim || tile_tok0 + kTile > tok_end, 0)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int lim = min(my_lim[rb], tok_end);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              xs[h][rb][q2][e] =
+                  tile_tok0 + 32 * h + 16 * q2 + 4 * g + e < lim ? xs[h][rb][q2][e] : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pe[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        float& y = xs[k >> 3][rb][(k >> 2) & 1][k & 3];
+        y = __builtin_fmaf(y, c, -msub[rb]);
+        pe[k] = fast_exp2(y);
+      }
+      float tsum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) tsum += pe[k];
+      const bool check = ref[rb] == kNegInf || !(tsum <= 256.f);  // 2^kSlack
+      if (__builtin_amdgcn_ballot_w64(check) != 0) {  // wave-uniform, rare
+        float tmax = kNegInf;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) tmax = __builtin_fmaxf(tmax, xs[k >> 3][rb][(k >> 2) & 1][k & 3]);
+        const bool raise = tmax > (ref[rb] == kNegInf ? kNegInf : kSlack);
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          float rmax = __builtin_fmaxf(tmax, shfl_xor(tmax, 16));
+          rmax = __builtin_fmaxf(rmax, shfl_xor(rmax, 32));
+          const float nref = __builtin_fmaxf(ref[rb], rmax + msub[rb]);
+          const float nsub = nref == kNegInf ? 0.f : nref;
+          const float shift = msub[rb] - nsub;
+          const float alpha = fast_exp2(shift);
+          ref[rb] = nref;
+          msub[rb] = nsub;
+          lsum[rb] *= alpha;
+          tsum = 0.f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            float& y = xs[k >> 3][rb][(k >> 2) & 1][k & 3];
+            y += shift;
+            pe[k] = fast_exp2(y);
+            tsum += pe[k];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ae = __builtin_bit_cast(
+                float,
+                __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+            for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb][e] *= ae;
+          }
+        }
+      }
+      lsum[rb] += tsum;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pw[h][rb][w] = f32x2_to_f16x2(pe[8 * h + 2 * w], pe[8 * h + 2 * w + 1]);
     }
   };
   const std::true_type f16v;
@@ -425,10 +486,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const int lbuf = team == 0 ? (kB + 1) % kNBuf : (kB + 2) % kNBuf;
     const bool load = lt < n_tiles;
     if (load) load_rows(tok_begin + lt * kTile, lbuf, vr);
-    if (active(t)) {
-      exponents(tok_begin + t * kTile, x);
-      weights_f16(x, pw);
-    }
+    if (active(t)) softmax_f16(tok_begin + t * kTile, x, pw);
     if (load) store_v(f16v, tok_begin + lt * kTile, lbuf, vr);
   };
   for (int t = 0;; t += kNBuf) {
