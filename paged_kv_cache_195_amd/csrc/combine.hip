@@ -2,9 +2,17 @@
 // (rocMLIR "Fix split-kv attention masking and sweep RMS", Technical Details,
 // host reference: the combine stage runs in f32 and casts back once).
 //
-// One wave per row: lanes reduce max and sum of the split LSEs, then walk the
-// head dimension.  Rows whose every split is empty (all LSE = -inf) get
-// output 0 and LSE -inf instead of a 0/0.
+// combine_row_kernel (S <= 256, Dv a multiple of 4, 16-byte aligned
+// partials -- every call the attention path makes): one workgroup per row.
+// Thread s holds split s's LSE; the workgroup reduces their max M, each
+// thread forms its split's weight exp(lse_s - M) once (kept in LDS), and the
+// threads then read the partials in 16-byte chunks, each thread a chunk of
+// the head dimension for every (256 / (Dv/4))-th split, several loads in
+// flight, before the split groups are summed through LDS.
+// combine_kernel (any other shape): one wave per row, lanes reduce max and
+// sum of the split LSEs, then walk the head dimension.
+// Rows whose every split is empty (all LSE = -inf) get output 0 and LSE -inf
+// instead of a 0/0.
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -53,30 +61,105 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (lane == 0 && lse != nullptr) lse[row] = mx + logf(wsum);
 }
 
+constexpr int kCombineThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void combine_row_kernel(
+    const float* __restrict__ part_out, const float* __restrict__ part_lse,
+    T* __restrict__ out, float* __restrict__ lse, int num_splits, int dv) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ float w_s[kCombineThreads];
+  __shared__ f32x4_t acc_s[kCombineThreads];
+  __shared__ float red[2][kCombineThreads / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t row = blockIdx.x;
+  const float* lr = part_lse + row * num_splits;
+  const float* orow = part_out + row * num_splits * dv;
+  T* dst = out + row * dv;
+
+  // M = max_s lse_s (thread s holds split s)
+  const float l = t < num_splits ? lr[t] : kNegInf;
+  const float wm = wave_max(l);
+  if (lane == 0) red[0][wave] = wm;
+  __syncthreads();
+  float mx = red[0][0];
+#pragma unroll
+  for (int k = 1; k < kCombineThreads / 64; ++k) mx = __builtin_fmaxf(mx, red[0][k]);
+  if (mx == kNegInf) {  // workgroup-uniform: every split is empty
+    for (int d = t; d < dv; d += kCombineThreads) dst[d] = from_float<T>(0.f);
+    if (t == 0 && lse != nullptr) lse[row] = kNegInf;
+    return;
+  }
+  const float w = t < num_splits ? expf(l - mx) : 0.f;
+  w_s[t] = w;
+  const float wsw = wave_sum(w);
+  if (lane == 0) red[1][wave] = wsw;
+  __syncthreads();
+  float wsum = red[1][0];
+#pragma unroll
+  for (int k = 1; k < kCombineThreads / 64; ++k) wsum += red[1][k];
+
+  // thread (sg, c): chunk c (4 floats) of every groups-th split from sg
+  const int nc = dv >> 2;
+  const int groups = kCombineThreads / nc;
+  const int c = t % nc, sg = t / nc;
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+  if (sg < groups) {
+#pragma unroll 4
+    for (int sp = sg; sp < num_splits; sp += groups) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(orow + static_cast<int64_t>(sp) * dv + 4 * c);
+      const float ws = w_s[sp];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(ws, v[i], a[i]);
+    }
+  }
+  acc_s[t] = a;
+  __syncthreads();
+  if (t < nc) {
+    f32x4_t r = acc_s[t];
+    for (int k = 1; k < groups; ++k) {
+      const f32x4_t q = acc_s[k * nc + t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] += q[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[4 * t + i] = from_float<T>(r[i] / wsum);
+  }
+  if (t == 0 && lse != nullptr) lse[row] = mx + logf(wsum);
+}
+
+template <typename T>
+hipError_t launch_combine_t(int rows, int num_splits, int dv, const float* part_out,
+                            const float* part_lse, T* out, float* lse, hipStream_t stream) {
+  const bool row_kernel = num_splits <= kCombineThreads && dv % 4 == 0 &&
+                          dv / 4 <= kCombineThreads &&
+                          (reinterpret_cast<uintptr_t>(part_out) & 15u) == 0;
+  if (row_kernel)
+    combine_row_kernel<T><<<dim3(rows), dim3(kCombineThreads), 0, stream>>>(
+        part_out, part_lse, out, lse, num_splits, dv);
+  else
+    combine_kernel<T><<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(part_out, part_lse, out,
+                                                                      lse, rows, num_splits, dv);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,
                           hipStream_t stream) {
-  const dim3 grid((rows + 3) / 4), block(256);
   switch (dtype) {
     case kF32:
-      combine_kernel<float><<<grid, block, 0, stream>>>(part_out, part_lse,
-                                                         static_cast<float*>(out), lse, rows,
-                                                         num_splits, head_dim_v);
-      break;
+      return launch_combine_t(rows, num_splits, head_dim_v, part_out, part_lse,
+                              static_cast<float*>(out), lse, stream);
     case kF16:
-      combine_kernel<f16_t><<<grid, block, 0, stream>>>(part_out, part_lse,
-                                                         static_cast<f16_t*>(out), lse, rows,
-                                                         num_splits, head_dim_v);
-      break;
+      return launch_combine_t(rows, num_splits, head_dim_v, part_out, part_lse,
+                              static_cast<f16_t*>(out), lse, stream);
     case kBF16:
-      combine_kernel<bf16_t><<<grid, block, 0, stream>>>(part_out, part_lse,
-                                                          static_cast<bf16_t*>(out), lse, rows,
-                                                          num_splits, head_dim_v);
-      break;
+      return launch_combine_t(rows, num_splits, head_dim_v, part_out, part_lse,
+                              static_cast<bf16_t*>(out), lse, stream);
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -237,22 +237,30 @@ def test_prefill_non_causal():
 
 
 # ----------------------------------------------------------------------------- combine
+# The first three shapes take the one-workgroup-per-row kernel (S <= 256, Dv a
+# multiple of 4 and at most 1024, 16-byte aligned partials), at its S and Dv limits;
+# the others take the one-wave-per-row kernel: S past 256, Dv not a multiple of 4,
+# Dv past 1024, and partials at an offset of one float.
+@pytest.mark.parametrize("rows,splits,dv,offset", [
+    (37, 6, 64, 0), (7, 256, 128, 0), (6, 3, 1024, 0),
+    (5, 300, 32, 0), (9, 3, 30, 0), (4, 5, 2048, 0), (11, 4, 64, 1)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
-def test_combine_direct(dtype):
-    say(f"combine {dtype}")
+def test_combine_direct(dtype, rows, splits, dv, offset):
+    say(f"combine {dtype} rows={rows} S={splits} Dv={dv} offset={offset}")
     g = torch.Generator().manual_seed(13)
-    rows, splits, dv = 37, 6, 64
     po = torch.randn(rows, splits, dv, generator=g)
     pl = torch.randn(rows, splits, generator=g) * 3
     pl[pl < -2.5] = -math.inf          # some empty splits
-    pl[5] = -math.inf                  # a row with no valid key at all
+    pl[rows // 2] = -math.inf          # a row with no valid key at all
     po[pl == -math.inf] = 0.0
-    out, lse = pa.combine(po.to(DEV), pl.to(DEV), dtype)
+    po_dev = torch.empty(po.numel() + offset, device=DEV)[offset:].view(rows, splits, dv)
+    po_dev.copy_(po)
+    out, lse = pa.combine(po_dev, pl.to(DEV), dtype)
     torch.cuda.synchronize()
     xo, xl = O.combine(po.double().numpy(), pl.double().numpy())
     assert_close(out, xo, dtype, "out")
     assert_close(lse, xl, torch.float32, "lse")
-    assert torch.all(out[5] == 0) and lse[5] == -math.inf
+    assert torch.all(out[rows // 2] == 0) and lse[rows // 2] == -math.inf
 
 
 # ----------------------------------------------------------------------------- full-size decode
