@@ -251,6 +251,13 @@ int pa_prefill_ex(const pa_shape* shape, const pa_options* options, const void* 
  *  rows        number of rows (> 0); num_splits S (> 0); head_dim_v Dv (> 0).
  *  part_out    [rows, S, Dv] float32.   part_lse [rows, S] float32.
  *  out         [rows, Dv] dtype.        lse      [rows] float32 or NULL.
+ *  stream      hipStream_t (NULL = default stream); the call is asynchronous.
+ *
+ * Pointers are device memory owned by the caller, each aligned to its element
+ * size (16-byte aligned partials with S <= 256 and Dv a multiple of 4, at
+ * most 1024, take the faster one-workgroup-per-row kernel).  Returns PA_OK,
+ * PA_EINVAL (bad dtype, a size <= 0, a NULL or misaligned pointer; nothing is
+ * launched) or PA_EHIP (launch failure).
  */
 int pa_combine(int32_t dtype, int32_t rows, int32_t num_splits, int32_t head_dim_v,
                const float* part_out, const float* part_lse, void* out, float* lse,

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   wsum = wave_sum(wsum);
   for (int d = lane; d < dv; d += 64) {
     float a = 0.f;
-    for (int s = 0; s < num_splits; ++s) a += expf(lr[s] - mx) * orow[s * dv + d];
+    for (int s = 0; s < num_splits; ++s)
+      a += expf(lr[s] - mx) * orow[static_cast<int64_t>(s) * dv + d];
     dst[d] = from_float<T>(a / wsum);
   }
   if (lane == 0 && lse != nullptr) lse[row] = mx + logf(wsum);

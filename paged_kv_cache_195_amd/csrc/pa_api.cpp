@@ -278,6 +278,10 @@ int pa_combine(int32_t dtype, int32_t rows, int32_t num_splits, int32_t head_dim
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_EINVAL;
   if (rows <= 0 || num_splits <= 0 || head_dim_v <= 0) return PA_EINVAL;
   if (part_out == nullptr || part_lse == nullptr || out == nullptr) return PA_EINVAL;
+  const uintptr_t out_align = dtype == PA_F32 ? 3u : 1u;
+  if (!aligned4(part_out) || !aligned4(part_lse) || !aligned4(lse) ||
+      (reinterpret_cast<uintptr_t>(out) & out_align) != 0)
+    return PA_EINVAL;
   const hipError_t err = pa::launch_combine(dtype, rows, num_splits, head_dim_v, part_out,
                                             part_lse, out, lse, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_EHIP;

@@ -150,6 +150,14 @@ def test_combine_validation():
     assert lib.pa_combine(2, 4, 0, 128, FAKE, FAKE, FAKE, None, None) == PA_EINVAL
     assert lib.pa_combine(2, 4, 2, 128, None, FAKE, FAKE, None, None) == PA_EINVAL
     assert lib.pa_combine(2, 4, 2, 128, FAKE, FAKE, None, None, None) == PA_EINVAL
+    # misaligned pointers: partials and lse need 4 bytes, a bf16 out 2, an f32 out 4
+    odd = ctypes.c_void_p(FAKE.value + 2)
+    assert lib.pa_combine(2, 4, 2, 128, odd, FAKE, FAKE, None, None) == PA_EINVAL
+    assert lib.pa_combine(2, 4, 2, 128, FAKE, odd, FAKE, None, None) == PA_EINVAL
+    assert lib.pa_combine(2, 4, 2, 128, FAKE, FAKE, FAKE, odd, None) == PA_EINVAL
+    assert lib.pa_combine(0, 4, 2, 128, FAKE, FAKE, odd, None, None) == PA_EINVAL
+    assert lib.pa_combine(2, 4, 2, 128, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 1), None,
+                          None) == PA_EINVAL
 
 
 def test_strerror():
