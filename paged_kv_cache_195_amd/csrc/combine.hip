@@ -2,13 +2,14 @@
 // (rocMLIR "Fix split-kv attention masking and sweep RMS", Technical Details,
 // host reference: the combine stage runs in f32 and casts back once).
 //
-// combine_row_kernel (S <= 256, Dv a multiple of 4, 16-byte aligned
-// partials -- every call the attention path makes): one workgroup per row.
-// Thread s holds split s's LSE; the workgroup reduces their max M, each
-// thread forms its split's weight exp(lse_s - M) once (kept in LDS), and the
-// threads then read the partials in 16-byte chunks, each thread a chunk of
-// the head dimension for every (256 / (Dv/4))-th split, several loads in
-// flight, before the split groups are summed through LDS.
+// combine_row_kernel (S <= 256, Dv a multiple of 4 and at most 1024,
+// 16-byte aligned partials -- every call the attention path makes): one
+// workgroup per row.  Each thread reads the partials in 16-byte chunks, a
+// chunk of the head dimension for every (256 / (Dv/4))-th split, issuing its
+// first four loads at entry; meanwhile every wave reduces the S LSEs to their
+// max M and the weights exp(lse_s - M) on its own (kept in its LDS row), so
+// no workgroup barrier precedes the weighted sum; the split groups are then
+// summed through LDS.
 // combine_kernel (any other shape): one wave per row, lanes reduce max and
 // sum of the split LSEs, then walk the head dimension.
 // Rows whose every split is empty (all LSE = -inf) get output 0 and LSE -inf
@@ -69,9 +70,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_row_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
     T* __restrict__ out, float* __restrict__ lse, int num_splits, int dv) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ float w_s[kCombineThreads];
+  constexpr int kWaves = kCombineThreads / 64;
+  constexpr int kLseSlots = kCombineThreads / 64;  // LSEs per lane (S <= 256)
+  constexpr int kPrefetch = 4;                     // partial chunks loaded up front
+  __shared__ float w_s[kWaves][kCombineThreads];   // each wave's own copy of the weights
   __shared__ f32x4_t acc_s[kCombineThreads];
-  __shared__ float red[2][kCombineThreads / 64];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int64_t row = blockIdx.x;
@@ -79,53 +82,81 @@ __global__ __launch_bounds__(kCombineThreads) void combine_row_kernel(
   const float* orow = part_out + row * num_splits * dv;
   T* dst = out + row * dv;
 
-  // M = max_s lse_s (thread s holds split s)
-  const float l = t < num_splits ? lr[t] : kNegInf;
-  const float wm = wave_max(l);
-  if (lane == 0) red[0][wave] = wm;
-  __syncthreads();
-  float mx = red[0][0];
+  // thread (sg, c): chunk c (4 floats) of splits sg, sg + groups, ...; the
+  // first kPrefetch of them are loaded before the weights are known, so their
+  // latency overlaps the LSE reductions
+  const int nc = dv >> 2;
+  const int groups = kCombineThreads / nc;
+  const int c = t % nc, sg = t / nc;
+  const bool active = sg < groups;
+  f32x4_t pv[kPrefetch];
 #pragma unroll
-  for (int k = 1; k < kCombineThreads / 64; ++k) mx = __builtin_fmaxf(mx, red[0][k]);
-  if (mx == kNegInf) {  // workgroup-uniform: every split is empty
+  for (int k = 0; k < kPrefetch; ++k) {
+    const int sp = sg + k * groups;
+    pv[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (active && sp < num_splits)
+      pv[k] = *reinterpret_cast<const f32x4_t*>(orow + static_cast<int64_t>(sp) * dv + 4 * c);
+  }
+
+  // every wave reduces all S LSEs itself (lane holds splits lane + 64 j), so
+  // no workgroup barrier is needed before the weighted sum
+  float l[kLseSlots];
+  float lm = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kLseSlots; ++j) {
+    const int sp = lane + 64 * j;
+    l[j] = sp < num_splits ? lr[sp] : kNegInf;
+    lm = __builtin_fmaxf(lm, l[j]);
+  }
+  const float mx = wave_max(lm);
+  if (mx == kNegInf) {  // the same in every wave: every split is empty
     for (int d = t; d < dv; d += kCombineThreads) dst[d] = from_float<T>(0.f);
     if (t == 0 && lse != nullptr) lse[row] = kNegInf;
     return;
   }
-  const float w = t < num_splits ? expf(l - mx) : 0.f;
-  w_s[t] = w;
-  const float wsw = wave_sum(w);
-  if (lane == 0) red[1][wave] = wsw;
-  __syncthreads();
-  float wsum = red[1][0];
+  float ws = 0.f;
 #pragma unroll
-  for (int k = 1; k < kCombineThreads / 64; ++k) wsum += red[1][k];
+  for (int j = 0; j < kLseSlots; ++j) {
+    const float w = l[j] == kNegInf ? 0.f : expf(l[j] - mx);
+    w_s[wave][lane + 64 * j] = w;
+    ws += w;
+  }
+  const float wsum = wave_sum(ws);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // thread (sg, c): chunk c (4 floats) of every groups-th split from sg
-  const int nc = dv >> 2;
-  const int groups = kCombineThreads / nc;
-  const int c = t % nc, sg = t / nc;
   f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-  if (sg < groups) {
-#pragma unroll 4
-    for (int sp = sg; sp < num_splits; sp += groups) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(orow + static_cast<int64_t>(sp) * dv + 4 * c);
-      const float ws = w_s[sp];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(ws, v[i], a[i]);
+  for (int k = 0; k < kPrefetch; ++k) {
+    const int sp = sg + k * groups;
+    const float w = active && sp < num_splits ? w_s[wave][sp] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(w, pv[k][i], a[i]);
+  }
+  if (active) {
+    for (int sp = sg + kPrefetch * groups; sp < num_splits; sp += groups) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(orow + static_cast<int64_t>(sp) * dv + 4 * c);
+      const float w = w_s[wave][sp];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(w, v[i], a[i]);
     }
   }
-  acc_s[t] = a;
-  __syncthreads();
-  if (t < nc) {
-    f32x4_t r = acc_s[t];
-    for (int k = 1; k < groups; ++k) {
-      const f32x4_t q = acc_s[k * nc + t];
+  if (groups > 1) {
+    acc_s[t] = a;
+    __syncthreads();
+    if (t < nc) {
+      a = acc_s[t];
+      for (int k = 1; k < groups; ++k) {
+        const f32x4_t q = acc_s[k * nc + t];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] += q[i];
+        for (int i = 0; i < 4; ++i) a[i] += q[i];
+      }
     }
+  }
+  if (t < nc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[4 * t + i] = from_float<T>(r[i] / wsum);
+    for (int i = 0; i < 4; ++i) dst[4 * t + i] = from_float<T>(a[i] / wsum);
   }
   if (t == 0 && lse != nullptr) lse[row] = mx + logf(wsum);
 }
