@@ -120,11 +120,18 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
       if (want > kMaxAutoSplits) want = kMaxAutoSplits;
       return want < 1 ? 1 : static_cast<int>(want);
     };
+    // Below one workgroup per compute unit, fewer kv heads per matrix-core
+    // workgroup (more waves on each head's pages) come first, down to two,
+    // then splits: at equal workgroup counts fewer splits are faster (graph-
+    // replayed bf16 decode, GQA 32/8: B=8, L=4096, S=32 x 8 heads 30.8 us,
+    // S=8 x 2 heads 27.3 us; B=16 50.4 -> 46.9 us; GQA 64/8, B=4, L=8192
+    // 37.3 -> 29.2 us)
+    while (plan.mfma && !plan.prefill && plan.heads_per_wg > 2 &&
+           units_for(plan.heads_per_wg) < kTargetWorkgroups)
+      plan.heads_per_wg /= 2;
     plan.num_splits = splits_for(plan.heads_per_wg);
-    // small batches, where the table width caps the splits: fewer kv heads per
-    // matrix-core workgroup (more waves on each head's pages) until the grid
-    // fills the GPU (B=1, L=4096, GQA 32/8: 34 -> 25 us; the ragged B=8 batch
-    // 25 -> 20 us)
+    // small batches, where the table width caps the splits: one kv head per
+    // workgroup if the grid is still short (B=1, L=4096, GQA 32/8: 34 -> 25 us)
     while (plan.mfma && !plan.prefill && plan.heads_per_wg > 1 &&
            units_for(plan.heads_per_wg) * plan.num_splits < kTargetWorkgroups) {
       plan.heads_per_wg /= 2;

@@ -99,7 +99,8 @@ def test_workspace_required_for_splits():
 
 def test_split_resolution():
     """Automatic S: at least 256 workgroups (one per compute unit), at most 64
-    and at most one split per 8 table slots (rounded up)."""
+    and at most one split per 8 table slots (rounded up); matrix-core decode
+    first lowers the kv heads per workgroup to two."""
     # Llama-3-8B decode shape: 256 workgroups of 16 waves (8 kv heads each) fill the GPU
     assert pa.resolve_num_splits(shape(), 0) == 1
     assert pa.workspace_bytes(shape(), 0) == 0
@@ -109,6 +110,15 @@ def test_split_resolution():
     assert pa.resolve_num_splits(s3, 0) == 8
     assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=8, block_table_stride=8), 0) == 1
     assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=9, block_table_stride=9), 0) == 2
+    # mid-size batches: kv heads per workgroup drop to two before the splits grow
+    # (B * Hkv / 2 * S = 256), S = 1 from 64 sequences on
+    assert pa.resolve_num_splits(shape(batch=8), 0) == 8
+    assert pa.resolve_num_splits(shape(batch=16), 0) == 4
+    assert pa.resolve_num_splits(shape(batch=32), 0) == 2
+    assert pa.resolve_num_splits(shape(batch=64), 0) == 1
+    assert pa.resolve_num_splits(shape(batch=128), 0) == 1
+    # one sequence: one kv head per workgroup and S = W / 8 = 32 splits
+    assert pa.resolve_num_splits(shape(batch=1), 0) == 32
     # Qwen3-235B decode shape (G = 16, matrix-core kernel, 4 kv heads per workgroup)
     s5 = shape(num_q_heads=64, num_kv_heads=4, max_pages_per_seq=512, block_table_stride=512,
                num_pages=131072)
