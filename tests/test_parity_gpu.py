@@ -162,6 +162,25 @@ def test_small_batch_decode_auto_plan(lens):
     assert_close(lse, xl, torch.float32, "lse")
 
 
+@pytest.mark.parametrize("batch,want_splits", [(8, 8), (16, 4), (32, 2), (64, 1), (128, 1)])
+def test_mid_batch_decode_auto_plan(batch, want_splits):
+    """Batches below one workgroup per compute unit at 8 kv heads per
+    workgroup: the automatic plan first drops to 2 kv heads per workgroup (4
+    at B=128), then splits; ragged lengths from 0 to the 64-slot table's
+    1024 tokens."""
+    say(f"mid-batch decode, automatic plan, B={batch}")
+    rng = np.random.default_rng(100 + batch)
+    lens = rng.integers(0, 1025, size=batch).tolist()
+    lens[0], lens[-1] = 1024, 0
+    w = make_custom("bf16", lens, 32, 8, 128, 16, width=64, seed=26, device=DEV)
+    shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
+    assert pa.resolve_num_splits(shape, 0) == want_splits
+    out, lse = run(w, 0)
+    xo, xl = oracle_full(w)
+    assert_close(out, xo, torch.bfloat16, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+
+
 def test_q_zero_closed_form():
     """q = 0: lse = ln(L) and out = mean of the valid V rows, for every split count."""
     say("q=0 closed form tiny_f32")
