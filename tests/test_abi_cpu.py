@@ -100,21 +100,24 @@ def test_workspace_required_for_splits():
 def test_split_resolution():
     """Automatic S: at least 256 workgroups (one per compute unit), at most 64
     and at most one split per 8 table slots (rounded up); matrix-core decode
-    first lowers the kv heads per workgroup to two."""
+    first lowers the kv heads per workgroup to two, then to one where that
+    gives S = 1 or where the splits sit at the table-width cap."""
     # Llama-3-8B decode shape: 256 workgroups of 16 waves (8 kv heads each) fill the GPU
     assert pa.resolve_num_splits(shape(), 0) == 1
     assert pa.workspace_bytes(shape(), 0) == 0
     assert pa.resolve_num_splits(shape(), 5) == 5
     # small batches split so the grid has enough workgroups, capped by the table width
+    # (the ragged batch's 63-slot table: at two kv heads per workgroup S = 8 would
+    # hit the one-split-per-8-slots cap, so one head per workgroup and S = 4)
     s3 = shape(batch=8, max_pages_per_seq=63, block_table_stride=63)
-    assert pa.resolve_num_splits(s3, 0) == 8
+    assert pa.resolve_num_splits(s3, 0) == 4
     assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=8, block_table_stride=8), 0) == 1
     assert pa.resolve_num_splits(shape(batch=8, max_pages_per_seq=9, block_table_stride=9), 0) == 2
     # mid-size batches: kv heads per workgroup drop to two before the splits grow
-    # (B * Hkv / 2 * S = 256), S = 1 from 64 sequences on
+    # (B * Hkv / 2 * S = 256); to one where that gives S = 1 (B = 32)
     assert pa.resolve_num_splits(shape(batch=8), 0) == 8
     assert pa.resolve_num_splits(shape(batch=16), 0) == 4
-    assert pa.resolve_num_splits(shape(batch=32), 0) == 2
+    assert pa.resolve_num_splits(shape(batch=32), 0) == 1
     assert pa.resolve_num_splits(shape(batch=64), 0) == 1
     assert pa.resolve_num_splits(shape(batch=128), 0) == 1
     # one sequence: one kv head per workgroup and S = W / 8 = 32 splits
@@ -224,5 +227,6 @@ def test_eight_bit_cache_validation():
     # 8-bit caches take the matrix-core kernel: 8 kv heads per workgroup at the
     # Llama-3-8B decode shape, 256 workgroups, so no split
     assert pa.resolve_num_splits(shape(kv_dtype=PA_I8), 0) == 1
+    # ... and the same plan as 16-bit caches at the ragged batch's shape
     assert pa.resolve_num_splits(shape(kv_dtype=PA_FP8_E4M3, batch=8, max_pages_per_seq=63,
-                                       block_table_stride=63), 0) == 8
+                                       block_table_stride=63), 0) == 4
