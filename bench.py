@@ -28,6 +28,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
+TIMING_BATCHES = 5
+# parity bar of the output against the f64 oracle: |y - x| <= atol + rtol * |x|
+TOLERANCE = {"f32": (1e-5, 1e-5), "f16": (2e-3, 2.0 ** -8), "bf16": (2e-3, 2.0 ** -8)}
+
+
+def _quantile(sorted_values, q):
+    """Linear-interpolation quantile of an ascending list."""
+    pos = q * (len(sorted_values) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(sorted_values) - 1)
+    return sorted_values[lo] + (pos - lo) * (sorted_values[hi] - sorted_values[lo])
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA peaks
 TRAFFIC_FILES = {
@@ -128,7 +139,8 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
                            w.table_host[b:b + 1].numpy(), np.array(w.seq_lens_host[b:b + 1]),
                            w.scale, w.causal)
 
-    done, elapsed, max_err, tokens, pages_read = [], 0.0, 0.0, 0, 0
+    atol, rtol = TOLERANCE[w.spec.dtype]
+    done, elapsed, max_err, tokens, pages_read, n_bad = [], 0.0, 0.0, 0, 0, 0
     with threadpool_limits(limits=1):
         while elapsed < budget_s and len(done) < batch:
             rows = order[len(done): len(done) + threads]
@@ -138,8 +150,10 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
                 res = list(ex.map(lambda b: one(b, kp, vp), rows))
             elapsed += time.perf_counter() - t0
             for b, (xo, _) in zip(rows, res):
-                y = out_gpu[b].float().cpu().numpy()
-                max_err = max(max_err, float(np.abs(y - xo[0, 0]).max()))
+                y = out_gpu[b].double().cpu().numpy()
+                err = np.abs(y - xo[0, 0])
+                max_err = max(max_err, float(err.max()))
+                n_bad += int((~(err <= atol + rtol * np.abs(xo[0, 0]))).sum())
                 tokens += w.seq_lens_host[b]
                 pages_read += -(-w.seq_lens_host[b] // ps)
             done.extend(rows)
@@ -155,6 +169,8 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
         "sample": f"{len(done)} of {batch} sequences (whole sequences, all heads), f64 NumPy, "
                   f"{threads} threads x 1 BLAS thread, {elapsed:.1f} s wall",
         "max_abs_err_vs_gpu": max_err,
+        "parity": {"ok": n_bad == 0, "elements_out_of_tolerance": n_bad,
+                   "atol": atol, "rtol": rtol},
     }
 
 
@@ -259,14 +275,25 @@ def main():
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
+    # One timed region of exactly `steps` steps, bracketed by synchronisations;
+    # events between TIMING_BATCHES equal batches (recorded without waiting)
+    # give the spread of the per-step time across the region.
     stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        run()
-    stop.record(stream)
+    n_batches = min(TIMING_BATCHES, args.steps)
+    bounds = [round(i * args.steps / n_batches) for i in range(n_batches + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_batches + 1)]
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    events[0].record(stream)
+    for i in range(n_batches):
+        for _ in range(bounds[i + 1] - bounds[i]):
+            run()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = events[0].elapsed_time(events[-1]) / args.steps
+    batch_us = sorted(events[i].elapsed_time(events[i + 1]) * 1e3 / (bounds[i + 1] - bounds[i])
+                      for i in range(n_batches))
+    spread = {"batches": n_batches, "median": round(_quantile(batch_us, 0.5), 2),
+              "p10": round(_quantile(batch_us, 0.1), 2), "p90": round(_quantile(batch_us, 0.9), 2)}
 
     nbytes = kv_bytes(w)
     spec = w.spec
@@ -278,6 +305,7 @@ def main():
             "metric": "paged causal prefill TFLOP/s (% of bf16 MFMA peak) + us/step",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+            "us_per_step_over_batches": spread,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": spec.dtype, "data": "synthetic: seeded N(0,1) q/k/v, seeded page permutation",
             "config": {"workload": f"{spec.name}: {spec.description}", "num_splits": splits,
@@ -297,6 +325,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_over_batches": spread,
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -330,6 +359,10 @@ def main():
         threads = max(1, min(len(os.sched_getaffinity(0)), 16))
         line["cpu_baseline"] = cpu_baseline(w, out[:, 0], args.cpu_budget, threads)
     print(json.dumps(line), flush=True)
+    if "cpu_baseline" in line and not line["cpu_baseline"]["parity"]["ok"]:
+        print("bench.py: the GPU output of the timed workload disagrees with the oracle",
+              file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
