@@ -102,7 +102,7 @@ typedef struct pa_shape {
 } pa_shape;
 
 /*
- * Supported envelope of this build (else PA_EUNSUPPORTED):
+ * Supported envelope of the compiled kernels (else PA_EUNSUPPORTED):
  *   dtype F32, F16 or BF16; D == Dv in {32, 64, 128}; page_size in {16, 32};
  *   any group size Hq / Hkv >= 1; B <= 65535 and Hkv <= 65535.
  *   8-bit caches (kv_dtype PA_I8 or PA_FP8_E4M3): dtype F16 or BF16 and

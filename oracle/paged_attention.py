@@ -18,19 +18,19 @@ What it computes, and where that is defined:
   kv_head, dim]``.  The rocm-libraries "one K/V resource per page" page
   (Motivation; Coverage, the in-page offset that must keep its kv-head term)
   fixes that a page holds all kv heads; token-major order inside the page is
-  this build's reading.
+  the reading taken here.
 * Block table entries at slot ``s < ceil(L / page_size)`` are physical page
   ids; later slots are never read (same page, Coverage: ragged lengths with an
   unmapped id in the table's tail).
 * Query head ``h`` reads kv head ``h // G`` with ``G = Hq / Hkv`` (grouped
-  query attention; contiguous groups is this build's reading).
+  query attention; contiguous groups is the reading taken here).
 * Causal masking is bottom-right aligned: query row ``i`` of ``Sq`` sits at key
   position ``L - Sq + i`` and sees keys ``j <= L - Sq + i``.  The rocMLIR
   "Fix split-kv attention masking" page (Technical Details, host reference:
   causal valid-split masking) defines validity per query row from that row's
   effective key length, including a prefix offset when one is given, and
   treats prefix-causal masking as causal.  With a per-sequence prefix offset
-  ``P_b`` (this build's reading of it), row ``i`` sits at key position
+  ``P_b`` (the reading taken here), row ``i`` sits at key position
   ``P_b + i`` instead, whatever the causal flag says.
 * Page-id range check (optional): the rocm-libraries "one K/V resource per
   page" page (Not in this PR; review, LOW findings) notes that page ids are
@@ -38,7 +38,7 @@ What it computes, and where that is defined:
   ``check_pages`` is that check: a sequence any of whose first
   ``ceil(L / page_size)`` ids lies outside ``[0, num_pages)``, or whose length
   lies outside ``[0, W * page_size]`` (the same bound on slot indices), is not attended
-  (this build's reading: it counts as empty, so its rows give ``(0, -inf)``),
+  (the reading taken here: it counts as empty, so its rows give ``(0, -inf)``),
   and the smallest such batch index is reported.
 * Split-KV: the key pages of a sequence are cut into ``S`` ranges of
   ``ceil(n / S)`` pages each, the last ranges clamped to ``n`` and possibly

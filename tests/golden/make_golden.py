@@ -96,7 +96,7 @@ FIXTURES = {
                     "list: the int8 e2e test) and i8 split-KV attention (rocMLIR 'Fix split-kv "
                     "attention masking and sweep RMS', Motivation); fp8 K/V loaders (rocm-libraries "
                     "'one K/V resource per page on the gfx942 2D i64 path', review). Scale "
-                    "granularity and the fp8 format are this build's reading.",
+                    "granularity and the fp8 format are the reading taken here.",
         "derivation": "Physical page 0 holds token 1, page 1 holds token 0. int8: k1 = ln3 * (1, 0), "
                       "k0 = 0 * (5, -3) = (0, 0), v1 = 0.25 * (0, 4) = (0, 1), v0 = -0.5 * (-2, 0) = "
                       "(1, 0). fp8 (0x38 = 1, 0x50 = 8, 0xC4 = -3, 0x80 = -0, 0x48 = 4, 0xB0 = -0.5): "
