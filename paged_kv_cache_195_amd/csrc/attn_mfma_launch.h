@@ -86,11 +86,35 @@ hipError_t launch_attn_mfma_t(const AttnParams& p, const AttnPlan& plan, int hea
   return hipErrorInvalidValue;
 }
 
-// 8-bit K/V codes: the MFMA kernel only (no shared-tile prefill variant).
+// 8-bit K/V codes, shared-tile prefill: the single-team kernel at both head
+// dims (its K tile passes through registers to be decoded, which the two-team
+// kernel's direct-to-LDS K loads cannot do).
+template <typename T, typename KV, int D, int PS>
+hipError_t launch_attn_prefill_q_dp(const AttnParams& p, const AttnPlan& plan, int batch,
+                                    hipStream_t stream) {
+  if (plan.waves != kPrefillWaves || plan.rows_per_wg != 16 * kPrefillRowBlocks * kPrefillWaves ||
+      plan.heads_per_wg != 1)
+    return hipErrorInvalidValue;
+  const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads, batch);
+  attn_prefill_kernel<T, D, PS, kPrefillWaves, kPrefillRowBlocks, KV>
+      <<<grid, dim3(kPrefillWaves * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+// 8-bit K/V codes: the MFMA kernel, or the shared-tile prefill kernel.
 template <typename T, typename KV>
 hipError_t launch_attn_mfma_q_kv(const AttnParams& p, const AttnPlan& plan, int head_dim,
                                  int page_size, int batch, hipStream_t stream) {
-  if (plan.prefill) return hipErrorInvalidValue;
+  if (plan.prefill) {
+    if (page_size == 16) {
+      if (head_dim == 64) return launch_attn_prefill_q_dp<T, KV, 64, 16>(p, plan, batch, stream);
+      if (head_dim == 128) return launch_attn_prefill_q_dp<T, KV, 128, 16>(p, plan, batch, stream);
+    } else if (page_size == 32) {
+      if (head_dim == 64) return launch_attn_prefill_q_dp<T, KV, 64, 32>(p, plan, batch, stream);
+      if (head_dim == 128) return launch_attn_prefill_q_dp<T, KV, 128, 32>(p, plan, batch, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (page_size == 16) {
     if (head_dim == 64) return launch_attn_mfma_dp<T, KV, 64, 16>(p, plan, batch, stream);
     if (head_dim == 128) return launch_attn_mfma_dp<T, KV, 128, 16>(p, plan, batch, stream);

@@ -60,10 +60,23 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
                         __builtin_bit_cast(float, w & 0xffff0000u));
 }
 
-template <typename T, int D, int PS, int NW, int RB>
+template <typename T, int D, int PS, int NW, int RB, typename KV = KvSame>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const AttnParams p) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(PS == 16 || PS == 32, "page size");
+  // 8-bit K/V codes (KvI8, KvFp8): both tiles pass through registers and are
+  // decoded exactly on their way into LDS -- K to the query type, V to f16 --
+  // so the LDS layout and the MFMA steps are those of 16-bit caches.  A
+  // 16-token sub-tile always lies in one page, so its K scale multiplies its
+  // scores, and its V scale joins its f16 weights as vs / vref, where vref is
+  // the largest |V scale| the wave has met (the accumulators are rescaled when
+  // it grows, like the running max), so a weight never exceeds its unscaled
+  // value and no scale overflows f16; the output is multiplied by vref at the
+  // end.  The weights keep f16's relative precision while vs / vref times the
+  // weight stays a normal f16 number: V scales within 2^6 of each other keep
+  // every weight down to 2^-8 exact to 2^-12; pages whose V scales are far
+  // below the largest lose relative precision in their (small) share.
+  constexpr bool kQuant = KvTraits<KV>::quant;
   constexpr int kTile = 64;                      // tokens per tile
   constexpr int kSub = kTile / 16;               // 16-token sub-tiles
   constexpr int kKSteps = D / 32;
@@ -78,7 +91,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   constexpr int kRowsPerWaveQ = 16 * RB;         // query rows per wave
   constexpr int kBuf = kTile * kRowBytes;        // one K or V tile in LDS
   constexpr float kSlack = 8.f;
-  constexpr bool kConvertV = std::is_same<T, bf16_t>::value;  // bf16 V goes to f16
+  constexpr bool kConvertV = !kQuant && std::is_same<T, bf16_t>::value;  // bf16 V goes to f16
+  constexpr int kCacheRowBytes = kQuant ? D : kRowBytes;  // a K or V row in the cache
+  constexpr int kCodeChunks = D / 16;                     // 16-byte chunks of a code row
+  constexpr int kRowsPerLoadQ = 64 / kCodeChunks;         // code rows per wave load
+  constexpr int kLoadsQ = kRowsPerWave / kRowsPerLoadQ;
+  static_assert(!kQuant || (kRowsPerWave % kRowsPerLoadQ == 0 && kLoadsQ >= 1 &&
+                            kRowsPerWave % 16 == 0),
+                "8-bit loads: whole code rows, whole 16-token sub-tiles per wave");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -176,11 +196,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
 
   PageTable pt;
   pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kRowBytes;
+  pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kCacheRowBytes;
   pt.n_pages = n_pages;
 
-  // ---- LDS: two K/V tile buffers (swizzled rows)
+  // ---- LDS: two K/V tile buffers (swizzled rows); for 8-bit codes also the
+  // K and V scales of each buffer's 16-token sub-tiles
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kBuf];
+  __shared__ float sub_scale[kQuant ? 2 * 2 * kSub : 1];  // [buf][K, V][sub-tile]
   lds_char* smem3 = (lds_char*)(smem);
   auto swz = [](int r, int cidx) __attribute__((always_inline)) {
     return r * kRowBytes + 16 * (cidx ^ ((2 * r) & (kChunks - 1)));
@@ -273,6 +295,68 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
     }
   };
 
+  // 8-bit codes: this wave's rows of a tile into registers (K and V codes,
+  // 16 per lane and load), with the K and V scales of their page; nothing is
+  // read (and the scales are 0) when the rows lie at or past tok_end.
+  typedef u32x4 QRegs[kLoadsQ];
+  const int lrq = lane / kCodeChunks;
+  const int lcq = lane % kCodeChunks;
+  auto load_tile_q = [&](int tile_tok0, QRegs& kr, QRegs& vr, float& ks, float& vs)
+                         __attribute__((always_inline)) {
+    const int row0 = kRowsPerWave * wave;
+    const int tok = tile_tok0 + row0;
+    ks = 0.f;
+    vs = 0.f;
+    if (tok < tok_end) {  // wave-uniform; one page per wave
+      const uint32_t pid = pt.id(tok / PS);
+      const int64_t base = pt.base_of(pid);
+      const int64_t si = static_cast<int64_t>(pid) * Hkv + kvh;
+      ks = p.k_scale[si];
+      vs = p.v_scale[si];
+      const int in_page = tok % PS;
+#pragma unroll
+      for (int j = 0; j < kLoadsQ; ++j) {
+        const uint32_t off = static_cast<uint32_t>(
+            ((in_page + j * kRowsPerLoadQ + lrq) * Hkv + kvh) * D + 16 * lcq);
+        kr[j] = *reinterpret_cast<const u32x4*>(kbase + base + off);
+        vr[j] = *reinterpret_cast<const u32x4*>(vbase + base + off);
+      }
+    }
+  };
+  // ... and from registers into LDS buffer `buf`, decoded (K to T, V to f16);
+  // rows at or past tok_end become zeros.  The wave that loaded a sub-tile's
+  // first row stores that sub-tile's scales.
+  auto store_tile_q = [&](int buf, int tile_tok0, const QRegs& kr, const QRegs& vr, float ks,
+                          float vs) __attribute__((always_inline)) {
+    if constexpr (kQuant) {
+      char* kb = smem + buf * 2 * kBuf;
+      char* vb = kb + kBuf;
+      const int row0 = kRowsPerWave * wave;
+#pragma unroll
+      for (int j = 0; j < kLoadsQ; ++j) {
+        const int r = row0 + j * kRowsPerLoadQ + lrq;
+        const bool keep = tile_tok0 + r < tok_end;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (keep) widen16<T, KV>(kr[j], lo, hi);
+        *reinterpret_cast<u32x4*>(kb + swz(r, 2 * lcq)) = lo;
+        *reinterpret_cast<u32x4*>(kb + swz(r, 2 * lcq + 1)) = hi;
+        lo = u32x4{0u, 0u, 0u, 0u};
+        hi = u32x4{0u, 0u, 0u, 0u};
+        if (keep) widen16<f16_t, KV>(vr[j], lo, hi);
+        *reinterpret_cast<u32x4*>(vb + swz(r, 2 * lcq)) = lo;
+        *reinterpret_cast<u32x4*>(vb + swz(r, 2 * lcq + 1)) = hi;
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kRowsPerWave / 16; ++k) {
+          sub_scale[(buf * 2 + 0) * kSub + row0 / 16 + k] = ks;
+          sub_scale[(buf * 2 + 1) * kSub + row0 / 16 + k] = vs;
+        }
+      }
+    }
+  };
+  float vref = 0.f, inv_vref = 0.f;  // 8-bit codes: largest |V scale| met so far
+
   // lsum[rb]: lane (g, li) sums row li's weights over its own tokens (the
   // four token groups are added at the end).  Summing on the vector ALUs
   // instead of with MFMAs against a block of ones saves 8 of 104 MFMAs per
@@ -287,6 +371,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   typedef float Scores[RB][2][4];
   // the S MFMAs of one half, both row blocks
   auto half_scores = [&](const char* kb, int h, Scores& x) __attribute__((always_inline)) {
+    const int buf = (kb - smem) / (2 * kBuf);
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       f32x4 sacc[RB];
@@ -299,10 +384,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) sacc[rb] = Mfma<T>::k32(ka, qb[rb][s], sacc[rb]);
       }
+      float ks = 1.f;
+      if constexpr (kQuant) ks = sub_scale[(buf * 2 + 0) * kSub + 2 * h + q2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[rb][q2][e] = sacc[rb][e];
+        for (int e = 0; e < 4; ++e) x[rb][q2][e] = kQuant ? sacc[rb][e] * ks : sacc[rb][e];
     }
   };
   // keys a row may not see, or outside the split, become -inf (a select, so
@@ -320,25 +407,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   };
   // weights 2^x of one half's exponents, 8 per row block (as f16, or as high
   // and low bf16 parts), their row sums, and O += P . V
-  auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x) __attribute__((always_inline)) {
+  auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x, const float* vfac)
+                     __attribute__((always_inline)) {
     constexpr bool kF16 = decltype(f16pv)::value;
     u32x4 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float pe[8];
+      float pe[8], pw[8];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e) {
           pe[4 * q2 + e] = fast_exp2(x[rb][q2][e]);  // x holds the exponent
+          pw[4 * q2 + e] = kQuant ? pe[4 * q2 + e] * vfac[2 * h + q2] : pe[4 * q2 + e];
+        }
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if constexpr (kF16) {
-          hi[w] = f32x2_to_f16x2(pe[2 * w], pe[2 * w + 1]);
+          hi[w] = f32x2_to_f16x2(pw[2 * w], pw[2 * w + 1]);
           lo[w] = 0u;
         } else {
-          Mfma<T>::split2(pe[2 * w], pe[2 * w + 1], hi[w], lo[w]);
+          Mfma<T>::split2(pw[2 * w], pw[2 * w + 1], hi[w], lo[w]);
         }
       }
       phi[rb] = u32x4{hi[0], hi[1], hi[2], hi[3]};
@@ -439,8 +529,34 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         }
       }
     }
-    half_pv(f16pv, vb3, 0, x0);
-    half_pv(f16pv, vb3, 1, x1);
+    float vfac[kSub];
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) vfac[k] = 1.f;
+    if constexpr (kQuant) {
+      // the tile's V scales relative to the largest |V scale| so far; when a
+      // larger one arrives, the accumulators move to the new reference
+      float vs[kSub], vmax = vref;
+#pragma unroll
+      for (int k = 0; k < kSub; ++k) {
+        vs[k] = sub_scale[(buf * 2 + 1) * kSub + k];
+        vmax = __builtin_fmaxf(vmax, __builtin_fabsf(vs[k]));
+      }
+      if (vmax > vref) {  // wave-uniform
+        const float ratio = vref / vmax;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int nb = 0; nb < kNBlocks; ++nb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[rb][nb][e] *= ratio;
+        vref = vmax;
+        inv_vref = 1.f / vmax;
+      }
+#pragma unroll
+      for (int k = 0; k < kSub; ++k) vfac[k] = vs[k] * inv_vref;
+    }
+    half_pv(f16pv, vb3, 0, x0, vfac);
+    half_pv(f16pv, vb3, 1, x1, vfac);
     __builtin_amdgcn_iglp_opt(1);
   };
 
@@ -483,7 +599,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       __syncthreads();  // the next tile has landed (the compiler waits for it) and this one is done
     }
   };
-  run(std::true_type());
+  if constexpr (kQuant) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ref[rb] = kNegInf;
+      msub[rb] = 0.f;
+      lsum[rb] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < kNBlocks; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    QRegs kr, vr;
+    float ks = 0.f, vs = 0.f;
+    if (n_tiles > 0) {
+      load_tile_q(tok_begin, kr, vr, ks, vs);
+      store_tile_q(0, tok_begin, kr, vr, ks, vs);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int tok0 = tok_begin + t * kTile;
+      const bool more = t + 1 < n_tiles;
+      if (more) load_tile_q(tok0 + kTile, kr, vr, ks, vs);
+      if (tok0 < wave_max_lim) compute_tile(std::true_type(), t & 1, tok0);
+      if (more) store_tile_q((t + 1) & 1, tok0 + kTile, kr, vr, ks, vs);
+      __syncthreads();  // the next tile is in LDS and this one is done
+    }
+  } else {
+    run(std::true_type());
+  }
   if constexpr (kConvertV) {
     // a V value beyond f16 range (or a non-finite input) left a non-finite
     // accumulator: 0 * inf and 0 * NaN are NaN
@@ -528,7 +670,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       const float lse = any ? (re + log2f(le)) * kLn2 : kNegInf;
       // one division per row, a multiply per element (within 1.5 ulp of
       // dividing each element; the division sequence is ~10 instructions)
-      const float inv = any ? 1.f / le : 0.f;
+      const float inv = any ? (kQuant ? vref : 1.f) / le : 0.f;
       if (S == 1) {
         T* dst = static_cast<T*>(p.out) + static_cast<int64_t>(rid) * D;
 #pragma unroll

@@ -81,12 +81,13 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   const bool quant = s->kv_dtype != 0;
   // 16-bit and 8-bit caches take the matrix-core kernels (8-bit codes are
   // dequantized exactly to the operand type); f32 caches the vector-ALU one.
-  // The shared-tile prefill variant reads 16-bit caches.
+  // The shared-tile prefill kernels read 16-bit caches and, in the
+  // single-team kernel, 8-bit codes.
   plan.mfma = quant || s->dtype != PA_F32;
-  plan.prefill = !quant && plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
+  plan.prefill = plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
-    plan.waves = pa::prefill_waves(s->head_dim_qk);
+    plan.waves = quant ? pa::kPrefillWaves : pa::prefill_waves(s->head_dim_qk);
     plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * plan.waves;
   } else if (plan.mfma) {
     plan.rows_per_wg = 16;

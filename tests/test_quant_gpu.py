@@ -58,6 +58,11 @@ CASES = [
     ("bf16", 64, 16, 8, 8, 1, [129, 64, 1], False),               # G = 1
     ("f16", 64, 32, 16, 2, 1, [500, 45], False),                  # G = 8
     ("bf16", 128, 16, 32, 8, 20, [100, 20, 333], True),           # causal prefill rows
+    # >= 64 rows per kv head: the shared-tile prefill kernel (codes decoded into LDS)
+    ("bf16", 128, 16, 32, 8, 64, [100, 64, 333], True),           # G = 4
+    ("f16", 64, 32, 16, 2, 40, [40, 300, 7], True),               # G = 8, page 32
+    ("bf16", 64, 16, 8, 8, 70, [70, 200], False),                 # G = 1, not causal
+    ("f16", 128, 32, 64, 4, 16, [500, 16, 0], True),              # G = 16, an empty one
 ]
 
 
@@ -88,6 +93,48 @@ def test_v_scale_doubling_is_exact(kind):
         b_out, b_lse, _ = run(w, splits)
         assert torch.equal(b_out.float(), 2.0 * a_out.float())
         assert torch.equal(a_lse, b_lse)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_prefill_v_scale_doubling_is_exact(kind):
+    """The shared-tile prefill kernel folds V scales into the f16 weights
+    relative to the largest one met: doubling every V scale doubles that
+    reference too, so the weights are unchanged and every output doubles bit
+    for bit, the LSE unchanged."""
+    say(f"prefill, V scale x2, {kind}")
+    w = make_custom("bf16", [300, 64, 700], 32, 8, 128, 16, seq_q=64, causal=True, seed=44,
+                    device=DEV, kv=kind)
+    v_scale = w.v_scale
+    for splits in (1, 3):
+        w.v_scale = v_scale
+        a_out, a_lse, _ = run(w, splits, True)
+        w.v_scale = v_scale * 2.0
+        b_out, b_lse, _ = run(w, splits, True)
+        assert torch.equal(b_out.float(), 2.0 * a_out.float())
+        assert torch.equal(a_lse, b_lse)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_wide_scales(kind, d):
+    """K and V scales of both signs, each multiplied by 2^-6 .. 1 per page and
+    kv head, in the shared-tile prefill kernel: the running V reference rises
+    several times, and weights scaled by vs / vref >= 2^-6 stay normal f16
+    numbers.  (The factors stay <= 1 so values keep the recipe's magnitude,
+    for which the absolute part of the parity bar is sized.)"""
+    say(f"prefill, wide-range scales, {kind}, D={d}")
+    w = make_custom("f16" if d == 64 else "bf16", [400, 130, 900], 16, 4, d, 16, seq_q=32,
+                    causal=True, seed=45, device=DEV, kv=kind)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(46)
+    for name in ("k_scale", "v_scale"):
+        sc = getattr(w, name)
+        mag = torch.exp2(torch.rand(sc.shape, generator=gen, device=DEV) * 6.0 - 6.0)
+        sign = torch.where(torch.rand(sc.shape, generator=gen, device=DEV) < 0.3, -1.0, 1.0)
+        setattr(w, name, sc * sign * mag)
+    for splits in (1, 3):
+        out, lse, ws = run(w, splits, True)
+        check(w, out, lse, ws, splits, True)
 
 
 @pytest.mark.parametrize("kind", KINDS)
