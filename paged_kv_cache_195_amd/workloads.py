@@ -119,6 +119,10 @@ WORKLOADS = {
                                          False, (0,), 10,
                                          "Llama-3-8B decode, fp8 E4M3 K/V codes, bf16 q/out B=256 "
                                          "Hq=32 Hkv=8 D=128 page16 Skv=4096", "fp8_e4m3"),
+    "prefill_b4_s1024_int8": WorkloadSpec("prefill_b4_s1024_int8", "bf16", 4, 1024, 32, 8, 128,
+                                          16, True, (0,), 11,
+                                          "causal prefill, int8 K/V codes, bf16 q/out B=4 "
+                                          "Sq=L=1024 Hq=32 Hkv=8 D=128 page16", "int8"),
 }
 
 KV_KINDS = ("int8", "fp8_e4m3")
