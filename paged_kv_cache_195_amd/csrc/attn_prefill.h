@@ -1,7 +1,8 @@
-// Paged prefill attention on the matrix cores (gfx950 MFMA), for 16-bit
-// caches when one kv head carries many query rows (a row is a (query
-// position, head of the group) pair).  Serves D = 64; D = 128 takes the
-// two-team kernel of attn_prefill_pp.h, which also uses this file's helpers.
+// Paged prefill attention on the matrix cores (gfx950 MFMA), when one kv
+// head carries many query rows (a row is a (query position, head of the
+// group) pair).  Serves 16-bit caches at D = 64 (D = 128 takes the two-team
+// kernel of attn_prefill_pp.h, which also uses this file's helpers) and
+// 8-bit K/V codes at D = 64 and 128.
 //
 // A workgroup owns 16 * RB * NW rows of one kv head; wave w owns RB blocks of
 // 16 rows.  The workgroup walks its split's keys in 64-token tiles.  Each
