@@ -84,7 +84,8 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   // The shared-tile prefill kernels read 16-bit caches and, in the
   // single-team kernel, 8-bit codes.
   plan.mfma = quant || s->dtype != PA_F32;
-  plan.prefill = plan.mfma && rows_per_kvh >= pa::kPrefillMinRows &&
+  plan.prefill = plan.mfma &&
+                 rows_per_kvh >= (quant ? pa::kPrefillMinRowsQuant : pa::kPrefillMinRows) &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
     plan.waves = quant ? pa::kPrefillWaves : pa::prefill_waves(s->head_dim_qk);

@@ -182,6 +182,25 @@ def test_mid_batch_decode_auto_plan(batch, want_splits):
     assert_close(lse, xl, torch.float32, "lse")
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv,seq_q", [
+    ("bf16", 128, 32, 1, 1),    # decode, G = 32: the two-team shared-tile kernel
+    ("f16", 128, 48, 1, 1),     # decode, G = 48
+    ("bf16", 64, 32, 1, 1),     # decode, G = 32, D = 64: the single-team kernel
+    ("bf16", 128, 32, 8, 8),    # 8 new queries per sequence at G = 4: 32 rows
+    ("f16", 64, 16, 8, 20)])    # 20 new queries at G = 2: 40 rows
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_32_to_63_rows_per_kv_head(dtype, d, hq, hkv, seq_q, splits):
+    """32 to 63 query rows per kv head take the shared-tile kernels with 16-bit
+    caches (most of their row blocks idle)."""
+    say(f"{dtype} D={d} Hq={hq} Hkv={hkv} Sq={seq_q} S={splits}: 32-63 rows per kv head")
+    w = make_custom(dtype, [300, 1000, 40, 0], hq, hkv, d, 16, seq_q=seq_q, causal=seq_q > 1,
+                    seed=27, device=DEV)
+    out, lse = run(w, splits)
+    xo, xl = oracle_full(w)
+    assert_close(out, xo, w.q.dtype, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+
+
 def test_q_zero_closed_form():
     """q = 0: lse = ln(L) and out = mean of the valid V rows, for every split count."""
     say("q=0 closed form tiny_f32")
