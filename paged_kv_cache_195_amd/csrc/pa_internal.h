@@ -36,7 +36,7 @@ struct AttnParams {
 // Launch shape chosen on the host.
 struct AttnPlan {
   bool mfma;         // matrix-core kernel (16-bit and 8-bit caches)
-  bool prefill;      // the shared-tile prefill variant of it (>= 64 rows per kv head)
+  bool prefill;      // a shared-tile kernel (kPrefillMinRows rows per kv head and more)
   int rows_per_wg;   // MR: query rows (position, head) per kv head in one workgroup
   int row_groups;    // ceil(rows_per_kvh / MR)
   int num_splits;    // S
