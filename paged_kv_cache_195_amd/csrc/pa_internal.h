@@ -92,12 +92,13 @@ constexpr int prefill_waves(int head_dim) {
 }
 // Query rows per kv head from which the shared-tile kernels take over from
 // the 16-row matrix-core kernel, which reads a kv head's pages once per 16
-// rows.  16-bit caches from 32 rows (graph-replayed bf16, B=256, L=4096:
-// GQA 32/1 167 -> 140 us, GQA 64/2 330 -> 266 us; GQA 48/1, B=32: 50 -> 25
+// rows.  16-bit caches as soon as a kv head has more than one 16-row block
+// (graph-replayed bf16, B=256, L=4096: GQA 24/1 168 -> 140 us, GQA 32/1 167
+// -> 140 us, GQA 40/2 324 -> 265 us; 5 new queries at GQA 32/8 21.7 -> 18.2
 // us); 8-bit codes from 64 (their decoding makes the shared tile's mostly
 // idle rows cost more: GQA 32/1 int8 107 us on the 16-row kernel, 149 us
 // shared).
-constexpr int kPrefillMinRows = 32;
+constexpr int kPrefillMinRows = 17;
 constexpr int kPrefillMinRowsQuant = 64;
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFp8E4M3 = 4 };

@@ -183,16 +183,19 @@ def test_mid_batch_decode_auto_plan(batch, want_splits):
 
 
 @pytest.mark.parametrize("dtype,d,hq,hkv,seq_q", [
-    ("bf16", 128, 32, 1, 1),    # decode, G = 32: the two-team shared-tile kernel
+    ("bf16", 128, 17, 1, 1),    # decode, G = 17: one row past a 16-row block
+    ("bf16", 128, 24, 1, 1),    # decode, G = 24: the two-team shared-tile kernel
+    ("bf16", 128, 32, 1, 1),    # decode, G = 32
     ("f16", 128, 48, 1, 1),     # decode, G = 48
     ("bf16", 64, 32, 1, 1),     # decode, G = 32, D = 64: the single-team kernel
-    ("bf16", 128, 32, 8, 8),    # 8 new queries per sequence at G = 4: 32 rows
+    ("bf16", 128, 32, 8, 5),    # 5 new queries per sequence at G = 4: 20 rows
+    ("bf16", 128, 32, 8, 8),    # 8 new queries at G = 4: 32 rows
     ("f16", 64, 16, 8, 20)])    # 20 new queries at G = 2: 40 rows
 @pytest.mark.parametrize("splits", [0, 1, 3])
-def test_32_to_63_rows_per_kv_head(dtype, d, hq, hkv, seq_q, splits):
-    """32 to 63 query rows per kv head take the shared-tile kernels with 16-bit
+def test_17_to_63_rows_per_kv_head(dtype, d, hq, hkv, seq_q, splits):
+    """17 to 63 query rows per kv head take the shared-tile kernels with 16-bit
     caches (most of their row blocks idle)."""
-    say(f"{dtype} D={d} Hq={hq} Hkv={hkv} Sq={seq_q} S={splits}: 32-63 rows per kv head")
+    say(f"{dtype} D={d} Hq={hq} Hkv={hkv} Sq={seq_q} S={splits}: 17-63 rows per kv head")
     w = make_custom(dtype, [300, 1000, 40, 0], hq, hkv, d, 16, seq_q=seq_q, causal=seq_q > 1,
                     seed=27, device=DEV)
     out, lse = run(w, splits)
