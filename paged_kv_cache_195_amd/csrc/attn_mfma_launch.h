@@ -3,38 +3,50 @@
 #pragma once
 
 #include "attn_mfma.h"
+#include "attn_mfma_rows.h"
 #include "attn_prefill.h"
 #include "attn_prefill_pp.h"
 
 namespace pa {
 
-template <typename T, typename KV, int D, int PS, int NW>
+template <typename T, typename KV, int D, int PS, int NW, int RB>
 hipError_t launch_attn_mfma_dpw(const AttnParams& p, const AttnPlan& plan, int batch,
                                 hipStream_t stream) {
-  if (plan.rows_per_wg != 16 || NW % plan.heads_per_wg != 0 ||
+  if (plan.rows_per_wg != 16 * RB || NW % plan.heads_per_wg != 0 ||
       p.num_kv_heads % plan.heads_per_wg != 0)
     return hipErrorInvalidValue;
   const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads / plan.heads_per_wg, batch);
   // 4-wave workgroups reserve unused LDS so that two, not three, stay resident
   // per compute unit: 8 waves per CU, as with 8-wave workgroups.  At 12 resident
   // waves the Qwen3-235B decode step took 726 us instead of 632.
-  constexpr int kStatic = mfma_static_lds<D, NW>();
+  constexpr int kStatic = RB == 1 ? mfma_static_lds<D, NW>() : mfma_rows_static_lds<D, NW, RB>();
   constexpr size_t kReserve = NW == 4 && kStatic < kMfmaLdsPerNarrowWg
                                   ? static_cast<size_t>(kMfmaLdsPerNarrowWg - kStatic)
                                   : 0;
-  attn_mfma_kernel<T, KV, D, PS, NW><<<grid, dim3(NW * 64), kReserve, stream>>>(p);
+  if constexpr (RB == 1)
+    attn_mfma_kernel<T, KV, D, PS, NW><<<grid, dim3(NW * 64), kReserve, stream>>>(p);
+  else
+    attn_mfma_rows_kernel<T, KV, D, PS, NW, RB><<<grid, dim3(NW * 64), kReserve, stream>>>(p);
   return hipGetLastError();
 }
 
-// 16-bit caches: 8 or 4 waves per workgroup; 8-bit codes: 8.
+// 16-bit caches: 8 or 4 waves per workgroup; 8-bit codes: 8.  One or two
+// blocks of 16 rows per wave (rows_per_wg 16 or 32).
+template <typename T, typename KV, int D, int PS, int NW>
+hipError_t launch_attn_mfma_dpn(const AttnParams& p, const AttnPlan& plan, int batch,
+                                hipStream_t stream) {
+  if (plan.rows_per_wg == 32) return launch_attn_mfma_dpw<T, KV, D, PS, NW, 2>(p, plan, batch, stream);
+  return launch_attn_mfma_dpw<T, KV, D, PS, NW, 1>(p, plan, batch, stream);
+}
+
 template <typename T, typename KV, int D, int PS>
 hipError_t launch_attn_mfma_dp(const AttnParams& p, const AttnPlan& plan, int batch,
                                hipStream_t stream) {
   if (plan.waves == kMfmaWaves)
-    return launch_attn_mfma_dpw<T, KV, D, PS, kMfmaWaves>(p, plan, batch, stream);
+    return launch_attn_mfma_dpn<T, KV, D, PS, kMfmaWaves>(p, plan, batch, stream);
   if constexpr (!KvTraits<KV>::quant) {
     if (plan.waves == kMfmaWavesNarrow)
-      return launch_attn_mfma_dpw<T, KV, D, PS, kMfmaWavesNarrow>(p, plan, batch, stream);
+      return launch_attn_mfma_dpn<T, KV, D, PS, kMfmaWavesNarrow>(p, plan, batch, stream);
   }
   return hipErrorInvalidValue;
 }

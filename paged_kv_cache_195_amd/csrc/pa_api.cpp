@@ -84,14 +84,28 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
   // The shared-tile prefill kernels read 16-bit caches and, in the
   // single-team kernel, 8-bit codes.
   plan.mfma = quant || s->dtype != PA_F32;
-  plan.prefill = plan.mfma &&
-                 rows_per_kvh >= (quant ? pa::kPrefillMinRowsQuant : pa::kPrefillMinRows) &&
+  // Decode (one query row per sequence) with up to 32 rows per kv head stays
+  // on the matrix-core kernel, two row blocks per wave from 17 rows, when the
+  // batch has at least kDecodeRowsMinUnits (sequence, kv head) pairs (bf16,
+  // L=4096: GQA 24/1 B=256 140 -> 95 us, B=128 67 -> 60 us, but B=64 36 ->
+  // 39 us, against the shared-tile kernel); several query rows per sequence
+  // take the shared-tile kernel from 17 rows (5 new queries at GQA 32/8: 18.2
+  // against 21.3 us).
+  const bool wide = static_cast<int64_t>(s->batch) * s->num_kv_heads >= pa::kDecodeRowsMinUnits;
+  const int64_t min_rows =
+      quant ? pa::kPrefillMinRowsQuant
+            : (s->seq_q == 1 && wide ? pa::kDecodeMinSharedRows : pa::kPrefillMinRows);
+  plan.prefill = plan.mfma && rows_per_kvh >= min_rows &&
                  (s->head_dim_qk == 64 || s->head_dim_qk == 128);
   if (plan.prefill) {
     plan.waves = quant ? pa::kPrefillWaves : pa::prefill_waves(s->head_dim_qk);
     plan.rows_per_wg = 16 * pa::kPrefillRowBlocks * plan.waves;
   } else if (plan.mfma) {
-    plan.rows_per_wg = 16;
+    // two 16-row blocks per wave when a kv head has more than 16 rows and the
+    // batch is wide: its pages are then read once per 32 rows instead of once
+    // per 16 (int8 GQA 32/1, B=256: 107 -> 71 us; at B=8, split 32 ways, one
+    // block per wave stays faster: 15.8 against 22.9 us)
+    plan.rows_per_wg = rows_per_kvh > 16 && wide ? 32 : 16;
     plan.waves = (!quant && s->num_kv_heads % 8 != 0) ? pa::kMfmaWavesNarrow : pa::kMfmaWaves;
   } else {
     plan.rows_per_wg = rows_per_wg(rows_per_kvh);

@@ -99,6 +99,13 @@ constexpr int prefill_waves(int head_dim) {
 // idle rows cost more: GQA 32/1 int8 107 us on the 16-row kernel, 149 us
 // shared).
 constexpr int kPrefillMinRows = 17;
+// Decode with 17 to 32 rows per kv head runs two 16-row blocks per wave on the
+// matrix-core kernel instead (attn_mfma_rows.h), the shared-tile kernels from
+// 33, when the batch holds at least kDecodeRowsMinUnits (sequence, kv head)
+// pairs; smaller batches, which split each sequence many ways, run faster on
+// the shared-tile kernels.
+constexpr int kDecodeMinSharedRows = 33;
+constexpr int kDecodeRowsMinUnits = 128;
 constexpr int kPrefillMinRowsQuant = 64;
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFp8E4M3 = 4 };
