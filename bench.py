@@ -209,7 +209,7 @@ def main():
                              "decode_b64_s8192_g8", "ragged_bf16", "tiny_f32",
                              "prefill_b4_s1024", "prefill_b1_s4096", "prefill_f16",
                              "llama3_8b_decode_int8", "llama3_8b_decode_fp8",
-                             "prefill_b4_s1024_int8"],
+                             "prefill_b4_s1024_int8", "decode_g32_b256"],
                     help="decode workload (the metric is quoted on llama3_8b_decode)")
     ap.add_argument("--variant", default=None,
                     help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "

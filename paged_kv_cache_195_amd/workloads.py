@@ -119,6 +119,10 @@ WORKLOADS = {
                                          False, (0,), 10,
                                          "Llama-3-8B decode, fp8 E4M3 K/V codes, bf16 q/out B=256 "
                                          "Hq=32 Hkv=8 D=128 page16 Skv=4096", "fp8_e4m3"),
+    "decode_g32_b256": WorkloadSpec("decode_g32_b256", "bf16", 256, 1, 32, 1, 128, 16, False,
+                                    (0,), 12,
+                                    "decode bf16 B=256 Hq=32 Hkv=1 D=128 page16 Skv=4096 "
+                                    "(group of 32 query heads per kv head)"),
     "prefill_b4_s1024_int8": WorkloadSpec("prefill_b4_s1024_int8", "bf16", 4, 1024, 32, 8, 128,
                                           16, True, (0,), 11,
                                           "causal prefill, int8 K/V codes, bf16 q/out B=4 "
@@ -268,6 +272,10 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         width = 512
         phys = 131328 if variant == "straddle" else (131072 if batch is None else max(1, b * 512))
     elif name == "llama3_70b_decode":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [4096] * b
+        width, phys = 256, b * 256
+    elif name == "decode_g32_b256":
         b = batch if batch is not None else spec.batch
         lens = list(seq_lens) if seq_lens is not None else [4096] * b
         width, phys = 256, b * 256
