@@ -12,6 +12,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 NEG_INF = "-inf"   # JSON has no infinity; readers map this string to -inf
+UNMAPPED = 0x7FFFFFFF  # block-table id of a slot that holds no page
 
 FIXTURES = {
     "hand_case": {
@@ -86,6 +87,135 @@ FIXTURES = {
                                [[math.log(2.0), 0.0]], [[math.log(2.0), math.log(2.0)]]]],
         "expected_out": [[[[1.0, 0.0]], [[0.5, 0.5]], [[1.0, 1.0]], [[1.75, 0.75]]]],
         "expected_lse": [[[0.0], [math.log(2.0)], [math.log(3.0)], [math.log(4.0)]]],
+    },
+    "split_paged_closed_form": {
+        "description": "Split-KV partition of multi-token pages: page size 4, two sequences of 10 "
+                       "and 5 tokens (3 and 2 pages) in a 5-slot table whose unused slots hold an "
+                       "unmapped id, S = 2 and S = 4, q = 0 so every valid score is 0 and each "
+                       "split's output is the mean of its V rows. Tokens past a sequence's length "
+                       "in its last page hold 1000 so that reading them changes the answer.",
+        "citation": "Split ranges: the iterations (pages) of one sequence are ceil-divided among "
+                    "the splits and each split's end is clamped to the sequence's own iteration "
+                    "count, so trailing splits may be empty: rocMLIR 'Fix split-kv attention "
+                    "masking and sweep RMS', Technical Details (non-causal split-KV iteration "
+                    "math) and Test Coverage (split-KV lowering and per-row mask tests). Tokens "
+                    "past the length are ignored and slots past a sequence's pages are never read: "
+                    "rocm-libraries 'one K/V resource per page on the gfx942 2D i64 path', Coverage.",
+        "derivation": "Sequence 0: L = 10, n = ceil(10/4) = 3 pages, V row of logical token t is "
+                      "(t, t^2). Sequence 1: L = 5, n = 2, V row (20 + t, 1). "
+                      "S = 2: sequence 0 has P = ceil(3/2) = 2 pages per split: split 0 = tokens "
+                      "0..7, mean (3.5, 140/8 = 17.5), lse ln 8; split 1 = page 2 clamped to L = "
+                      "tokens 8, 9, mean (8.5, (64+81)/2 = 72.5), lse ln 2. Sequence 1 has P = "
+                      "ceil(2/2) = 1: split 0 = tokens 0..3, (21.5, 1), ln 4; split 1 = token 4, "
+                      "(24, 1), ln 1 = 0. "
+                      "S = 4: sequence 0, P = 1: tokens 0..3 (1.5, 14/4 = 3.5) ln 4; tokens 4..7 "
+                      "(5.5, 126/4 = 31.5) ln 4; tokens 8, 9 (8.5, 72.5) ln 2; split 3 empty "
+                      "(0, 0), -inf. Sequence 1, P = 1: (21.5, 1) ln 4; (24, 1) 0; splits 2 and 3 "
+                      "empty. "
+                      "Unsplit: sequence 0 mean of tokens 0..9 (4.5, 285/10 = 28.5), lse ln 10; "
+                      "sequence 1 (22, 1), ln 5. "
+                      "Splitting by ceil(L/S) tokens instead (S = 2: 5 tokens each) would give "
+                      "ln 5 twice; sizing splits by the table width (P = ceil(5/2) = 3) would put "
+                      "all of sequence 0 in split 0.",
+        "dtype": "f32", "page_size": 4, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": False,
+        "q": [[[[0.0, 0.0]]], [[[0.0, 0.0]]]],
+        # physical page p holds [4 tokens][1 kv head][2 dims]; sequence 0 uses pages 2, 0, 4
+        # (tokens 0-3, 4-7, 8-11 with 10 and 11 past L), sequence 1 uses pages 1, 3
+        # (tokens 0-3, 4-7 with 5-7 past L)
+        "k_cache_pages": [
+            [[[0.5, -1.0]], [[2.0, 0.25]], [[-3.0, 1.0]], [[0.0, 4.0]]],
+            [[[1.0, 1.0]], [[-2.0, 0.5]], [[0.75, -0.5]], [[3.0, 3.0]]],
+            [[[-1.0, 2.0]], [[0.125, 0.0]], [[5.0, -5.0]], [[-0.25, 1.5]]],
+            [[[2.5, -2.5]], [[1000.0, 1000.0]], [[1000.0, 1000.0]], [[1000.0, 1000.0]]],
+            [[[-0.5, 0.5]], [[1.5, -1.5]], [[1000.0, 1000.0]], [[1000.0, 1000.0]]],
+        ],
+        "v_cache_pages": [
+            [[[4.0, 16.0]], [[5.0, 25.0]], [[6.0, 36.0]], [[7.0, 49.0]]],
+            [[[20.0, 1.0]], [[21.0, 1.0]], [[22.0, 1.0]], [[23.0, 1.0]]],
+            [[[0.0, 0.0]], [[1.0, 1.0]], [[2.0, 4.0]], [[3.0, 9.0]]],
+            [[[24.0, 1.0]], [[1000.0, 1000.0]], [[1000.0, 1000.0]], [[1000.0, 1000.0]]],
+            [[[8.0, 64.0]], [[9.0, 81.0]], [[1000.0, 1000.0]], [[1000.0, 1000.0]]],
+        ],
+        "block_table": [[2, 0, 4, UNMAPPED, UNMAPPED], [1, 3, UNMAPPED, UNMAPPED, UNMAPPED]],
+        "seq_lens": [10, 5],
+        "splits": {
+            "2": {
+                "expected_part_out": [[[[[3.5, 17.5], [8.5, 72.5]]]],
+                                      [[[[21.5, 1.0], [24.0, 1.0]]]]],
+                "expected_part_lse": [[[[math.log(8.0), math.log(2.0)]]],
+                                      [[[math.log(4.0), 0.0]]]],
+            },
+            "4": {
+                "expected_part_out": [[[[[1.5, 3.5], [5.5, 31.5], [8.5, 72.5], [0.0, 0.0]]]],
+                                      [[[[21.5, 1.0], [24.0, 1.0], [0.0, 0.0], [0.0, 0.0]]]]],
+                "expected_part_lse": [[[[math.log(4.0), math.log(4.0), math.log(2.0), NEG_INF]]],
+                                      [[[math.log(4.0), 0.0, NEG_INF, NEG_INF]]]],
+            },
+        },
+        "expected_out": [[[[4.5, 28.5]]], [[[22.0, 1.0]]]],
+        "expected_lse": [[[math.log(10.0)]], [[math.log(5.0)]]],
+    },
+    "split_paged_causal": {
+        "description": "Causal prefill over multi-token pages with split-KV: page size 2, Sq = L = 5 "
+                       "(3 pages) in a 4-slot table with an unmapped tail, S = 2 and S = 3, q = 0. "
+                       "Early rows see nothing of the later splits, which must give (0, -inf).",
+        "citation": "Ceil-divided, clamped split ranges (rocMLIR 'Fix split-kv attention masking and "
+                    "sweep RMS', Technical Details) and per-row causal validity from the row's "
+                    "effective key length, with fully masked partitions contributing zero (same "
+                    "page, Technical Details and the host reference's causal valid-split masking).",
+        "derivation": "V row of logical token t is (t, 1); row i sees keys 0..i. S = 2: P = "
+                      "ceil(3/2) = 2 pages, split 0 = tokens 0..3, split 1 = token 4 (token 5 of "
+                      "the last page is past L). Row i < 4: split 0 = mean of 0..i = (i/2, 1), "
+                      "lse ln(i+1); split 1 empty (0, 0), -inf. Row 4: split 0 (1.5, 1) ln 4; "
+                      "split 1 (4, 1) ln 1 = 0. S = 3: P = 1, splits = tokens {0,1}, {2,3}, {4}. "
+                      "Row 0: (0,1) 0; empty; empty. Row 1: (0.5,1) ln 2; empty; empty. Row 2: "
+                      "(0.5,1) ln 2; (2,1) 0; empty. Row 3: (0.5,1) ln 2; (2.5,1) ln 2; empty. "
+                      "Row 4: (0.5,1) ln 2; (2.5,1) ln 2; (4,1) 0. Combined row i: (i/2, 1), "
+                      "lse ln(i+1). Splitting by ceil(L/S) tokens (S = 2: 3 tokens) would give "
+                      "row 3 a split 1 of token 3.",
+        "dtype": "f32", "page_size": 2, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 2,
+        "scale": 1.0, "causal": True,
+        "q": [[[[0.0, 0.0]], [[0.0, 0.0]], [[0.0, 0.0]], [[0.0, 0.0]], [[0.0, 0.0]]]],
+        # the table is [1, 2, 0, unmapped]: page 1 holds tokens 0-1, page 2 tokens 2-3,
+        # page 0 token 4 and (past L) token 5
+        "k_cache_pages": [
+            [[[0.5, 0.5]], [[1000.0, 1000.0]]],
+            [[[-1.0, 2.0]], [[3.0, -3.0]]],
+            [[[0.25, 0.0]], [[2.0, 1.0]]],
+        ],
+        "v_cache_pages": [
+            [[[4.0, 1.0]], [[1000.0, 1000.0]]],
+            [[[0.0, 1.0]], [[1.0, 1.0]]],
+            [[[2.0, 1.0]], [[3.0, 1.0]]],
+        ],
+        "block_table": [[1, 2, 0, UNMAPPED]],
+        "seq_lens": [5],
+        "splits": {
+            "2": {
+                "expected_part_out": [[[[[0.0, 1.0], [0.0, 0.0]]], [[[0.5, 1.0], [0.0, 0.0]]],
+                                       [[[1.0, 1.0], [0.0, 0.0]]], [[[1.5, 1.0], [0.0, 0.0]]],
+                                       [[[1.5, 1.0], [4.0, 1.0]]]]],
+                "expected_part_lse": [[[[0.0, NEG_INF]], [[math.log(2.0), NEG_INF]],
+                                       [[math.log(3.0), NEG_INF]], [[math.log(4.0), NEG_INF]],
+                                       [[math.log(4.0), 0.0]]]],
+            },
+            "3": {
+                "expected_part_out": [[[[[0.0, 1.0], [0.0, 0.0], [0.0, 0.0]]],
+                                       [[[0.5, 1.0], [0.0, 0.0], [0.0, 0.0]]],
+                                       [[[0.5, 1.0], [2.0, 1.0], [0.0, 0.0]]],
+                                       [[[0.5, 1.0], [2.5, 1.0], [0.0, 0.0]]],
+                                       [[[0.5, 1.0], [2.5, 1.0], [4.0, 1.0]]]]],
+                "expected_part_lse": [[[[0.0, NEG_INF, NEG_INF]],
+                                       [[math.log(2.0), NEG_INF, NEG_INF]],
+                                       [[math.log(2.0), 0.0, NEG_INF]],
+                                       [[math.log(2.0), math.log(2.0), NEG_INF]],
+                                       [[math.log(2.0), math.log(2.0), 0.0]]]],
+            },
+        },
+        "expected_out": [[[[0.0, 1.0]], [[0.5, 1.0]], [[1.0, 1.0]], [[1.5, 1.0]], [[2.0, 1.0]]]],
+        "expected_lse": [[[0.0], [math.log(2.0)], [math.log(3.0)], [math.log(4.0)],
+                          [math.log(5.0)]]],
     },
     "quantized_hand_case": {
         "description": "The hand case above with K and V stored as 8-bit codes and one scale per "

@@ -82,6 +82,28 @@ def check_golden_causal():
     check_golden_split("causal_masked_split")
 
 
+def check_golden_split_paged(names=("split_paged_closed_form", "split_paged_causal")):
+    """Multi-token pages, a table wider than the sequences' page counts and
+    ragged lengths: the partials of every listed split count, their combine
+    and the unsplit result against the fixtures' closed forms."""
+    for name in names:
+        with open(os.path.join(GOLDEN, name + ".json")) as f:
+            raw = json.load(f)
+        g = load_golden(name)
+        args = (g["q"], g["k_cache_pages"], g["v_cache_pages"], g["block_table"],
+                g["seq_lens"], g["scale"], g["causal"])
+        for s, exp in raw["splits"].items():
+            po, pl = O.split_partials(*args, int(s))
+            _close(po, np.array(_to_float(exp["expected_part_out"])))
+            _close(pl, np.array(_to_float(exp["expected_part_lse"])))
+            out, lse = O.combine(po, pl)
+            _close(out, g["expected_out"])
+            _close(lse, g["expected_lse"])
+        out, lse = O.attention(*args)
+        _close(out, g["expected_out"])
+        _close(lse, g["expected_lse"])
+
+
 # ----------------------------------------------------------------------------- problems
 def random_problem(rng, batch=3, seq_q=1, hq=4, hkv=2, d=3, dv=None, ps=2, lens=None,
                    width=None, extra_pages=3, poison=True):
@@ -497,6 +519,7 @@ ALL_CHECKS = [
     check_golden_hand,
     check_golden_split,
     check_golden_causal,
+    check_golden_split_paged,
     check_brute_force,
     check_q_zero_decode,
     check_q_zero_causal,

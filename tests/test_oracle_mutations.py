@@ -135,6 +135,40 @@ def split_floor_division(n_pages, num_splits):
     return [(min(s * per, n_pages), min((s + 1) * per, n_pages)) for s in range(int(num_splits))]
 
 
+def split_partials_token_granular(q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                                  num_splits, prefix_offset=None):
+    """Splits cut by ceil(L / S) tokens instead of whole pages: the same caches
+    re-expressed as one-token pages, so the page-granular code splits tokens."""
+    ps = k_cache.shape[1]
+    k1 = np.asarray(k_cache).reshape((-1, 1) + k_cache.shape[2:])
+    v1 = np.asarray(v_cache).reshape((-1, 1) + v_cache.shape[2:])
+    bt = np.asarray(block_table, dtype=np.int64)
+    table = np.zeros((bt.shape[0], bt.shape[1] * ps), dtype=np.int64)
+    for b, length in enumerate(seq_lens):
+        for t in range(int(length)):
+            table[b, t] = bt[b, t // ps] * ps + t % ps
+    return _orig_split_partials(q, k1, v1, table, seq_lens, scale, causal, num_splits,
+                                prefix_offset)
+
+
+def split_partials_width_sized(q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                               num_splits, prefix_offset=None):
+    """Pages per split sized by the table width W instead of the sequence's own
+    page count n (ends still clamped to n)."""
+    width = np.asarray(block_table).shape[1]
+
+    def by_width(n_pages, splits):
+        return [(min(a, n_pages), min(b, n_pages)) for a, b in _orig_split_ranges(width, splits)]
+
+    saved = O.split_page_ranges
+    O.split_page_ranges = by_width
+    try:
+        return _orig_split_partials(q, k_cache, v_cache, block_table, seq_lens, scale, causal,
+                                    num_splits, prefix_offset)
+    finally:
+        O.split_page_ranges = saved
+
+
 def combine_lse_double_max(part_out, part_lse):
     out, lse = _orig_combine(part_out, part_lse)
     m = np.max(np.asarray(part_lse), axis=-1)
@@ -142,6 +176,8 @@ def combine_lse_double_max(part_out, part_lse):
 
 
 _orig_combine = O.combine
+_orig_split_partials = O.split_partials
+_orig_split_ranges = O.split_page_ranges
 
 MUTATIONS = [
     ("kv_head_of", lambda q_head, group: q_head % group if group > 1 else q_head),
@@ -166,6 +202,8 @@ MUTATIONS = [
     ("dequantize_cache", dequantize_pages_reversed),
     ("gather_logical", gather_reversed_pages),
     ("split_page_ranges", split_floor_division),
+    ("split_partials", split_partials_token_granular),
+    ("split_partials", split_partials_width_sized),
     ("combine", combine_lse_double_max),
 ]
 
