@@ -278,6 +278,33 @@ size_t pa_workspace_bytes(const pa_shape* shape, int num_splits);
  * Negative pa_status for an invalid shape or num_splits. */
 int pa_resolve_num_splits(const pa_shape* shape, int num_splits);
 
+/* Kernel families a call can take (pa_plan_info.kernel). */
+typedef enum pa_kernel {
+  PA_KERNEL_VALU = 0,             /* vector-ALU kernel (f32 caches)                     */
+  PA_KERNEL_MFMA = 1,             /* matrix-core kernel, one 16-row block per wave      */
+  PA_KERNEL_MFMA_TWO_BLOCKS = 2,  /* matrix-core kernel, two 16-row blocks per wave
+                                     sharing each staged K/V tile                       */
+  PA_KERNEL_SHARED_TILE = 3,      /* shared-tile kernel, one team of waves              */
+  PA_KERNEL_SHARED_TILE_TEAMS = 4 /* shared-tile kernel, two teams in opposite phases   */
+} pa_kernel;
+
+/* Launch plan of a pa_decode / pa_prefill call (pa_describe_plan). */
+typedef struct pa_plan_info {
+  int32_t kernel;              /* a pa_kernel                                         */
+  int32_t num_splits;          /* S the call uses (as pa_resolve_num_splits)          */
+  int32_t rows_per_workgroup;  /* query rows of one kv head per workgroup             */
+  int32_t row_groups;          /* ceil(Sq * Hq / Hkv / rows_per_workgroup)            */
+  int32_t waves;               /* waves (64 lanes each) per workgroup                 */
+  int32_t kv_heads_per_workgroup;
+} pa_plan_info;
+
+/* The plan a call with this shape and `num_splits` (0 = auto) takes, written
+ * to *info.  Host-only: it depends on the shape alone, launches nothing and
+ * touches no device memory.  Returns PA_OK, or a negative pa_status for an
+ * invalid shape or num_splits, or a NULL info (then *info is not written).
+ * Shape checks are those of pa_prefill (any seq_q). */
+int pa_describe_plan(const pa_shape* shape, int num_splits, pa_plan_info* info);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pa_strerror(int status);
 

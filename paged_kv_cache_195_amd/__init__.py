@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     PaShape,
     combine,
     decode,
+    describe_plan,
     load_library,
     make_shape,
     prefill,

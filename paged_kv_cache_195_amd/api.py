@@ -25,7 +25,10 @@ KV_CODE = {torch.int8: PA_I8, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 # The functions include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_prefill", "pa_decode_ex", "pa_prefill_ex", "pa_combine",
-           "pa_workspace_bytes", "pa_resolve_num_splits", "pa_strerror")
+           "pa_workspace_bytes", "pa_resolve_num_splits", "pa_describe_plan", "pa_strerror")
+# pa_kernel
+KERNEL_NAMES = {0: "valu", 1: "mfma", 2: "mfma_two_blocks", 3: "shared_tile",
+                4: "shared_tile_teams"}
 
 
 class PaShape(ctypes.Structure):
@@ -44,6 +47,19 @@ class PaShape(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("block_table_stride", ctypes.c_int64),
         ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+class PaPlanInfo(ctypes.Structure):
+    """Mirror of ``pa_plan_info``."""
+
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("rows_per_workgroup", ctypes.c_int32),
+        ("row_groups", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("kv_heads_per_workgroup", ctypes.c_int32),
     ]
 
 
@@ -90,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_workspace_bytes.restype = sz
     lib.pa_resolve_num_splits.argtypes = [shape_p, ctypes.c_int]
     lib.pa_resolve_num_splits.restype = ctypes.c_int
+    lib.pa_describe_plan.argtypes = [shape_p, ctypes.c_int, ctypes.POINTER(PaPlanInfo)]
+    lib.pa_describe_plan.restype = ctypes.c_int
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.pa_strerror.restype = ctypes.c_char_p
     _lib, _lib_path = lib, path
@@ -275,6 +293,17 @@ def workspace_bytes(shape: PaShape, num_splits: int = 0) -> int:
 
 def resolve_num_splits(shape: PaShape, num_splits: int = 0) -> int:
     return int(_current().pa_resolve_num_splits(ctypes.byref(shape), int(num_splits)))
+
+
+def describe_plan(shape: PaShape, num_splits: int = 0) -> dict:
+    """The launch plan of a call (``pa_describe_plan``): kernel name, split
+    count, rows per workgroup, row groups, waves, kv heads per workgroup."""
+    info = PaPlanInfo()
+    _check(_current().pa_describe_plan(ctypes.byref(shape), int(num_splits), ctypes.byref(info)),
+           "pa_describe_plan")
+    return {"kernel": KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
+            "rows_per_workgroup": info.rows_per_workgroup, "row_groups": info.row_groups,
+            "waves": info.waves, "kv_heads_per_workgroup": info.kv_heads_per_workgroup}
 
 
 def split_views(workspace: torch.Tensor, rows: int, num_splits: int, head_dim_v: int):

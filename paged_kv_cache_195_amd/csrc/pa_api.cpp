@@ -338,6 +338,28 @@ int pa_resolve_num_splits(const pa_shape* shape, int num_splits) {
   return plan_for(shape, num_splits).num_splits;
 }
 
+int pa_describe_plan(const pa_shape* shape, int num_splits, pa_plan_info* info) {
+  if (info == nullptr) return PA_EINVAL;
+  int st = check_shape(shape, false);
+  if (st != PA_OK) return st;
+  st = check_splits(num_splits);
+  if (st != PA_OK) return st;
+  const pa::AttnPlan plan = plan_for(shape, num_splits);
+  int kernel = PA_KERNEL_VALU;
+  if (plan.prefill)
+    kernel = plan.waves == pa::kPrefillTeamWaves ? PA_KERNEL_SHARED_TILE_TEAMS
+                                                 : PA_KERNEL_SHARED_TILE;
+  else if (plan.mfma)
+    kernel = plan.rows_per_wg == 32 ? PA_KERNEL_MFMA_TWO_BLOCKS : PA_KERNEL_MFMA;
+  info->kernel = kernel;
+  info->num_splits = plan.num_splits;
+  info->rows_per_workgroup = plan.rows_per_wg;
+  info->row_groups = plan.row_groups;
+  info->waves = plan.waves;
+  info->kv_heads_per_workgroup = plan.heads_per_wg;
+  return PA_OK;
+}
+
 const char* pa_strerror(int status) {
   switch (status) {
     case PA_OK: return "success";

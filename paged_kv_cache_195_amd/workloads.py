@@ -46,6 +46,12 @@ Workloads (``WORKLOADS``):
                     page 16.
 ``llama3_8b_decode_int8`` / ``llama3_8b_decode_fp8``  the Llama-3-8B decode
                     shape with 8-bit K/V codes (1 GiB per cache).
+``decode_past_4gib`` B=32, Hq=32, Hkv=8, D=128, page 16, L=4096 over caches of
+                    131,200 pages of 32 KiB (4 GiB + 4 MiB each): every page
+                    that starts at or past byte 2^32 (ids 131,072..131,199),
+                    and the page that ends there (131,071), is referenced, the
+                    rest of the 8,192 referenced pages drawn at random below;
+                    unreferenced pages hold NaN.
 
 8-bit caches (``kv="int8"`` or ``kv="fp8_e4m3"``): K and V hold codes drawn
 from the same seeded normals -- int8 as round(32 x) clamped to [-127, 127],
@@ -123,6 +129,10 @@ WORKLOADS = {
                                     (0,), 12,
                                     "decode bf16 B=256 Hq=32 Hkv=1 D=128 page16 Skv=4096 "
                                     "(group of 32 query heads per kv head)"),
+    "decode_past_4gib": WorkloadSpec("decode_past_4gib", "bf16", 32, 1, 32, 8, 128, 16, False,
+                                     (0,), 13,
+                                     "decode bf16 B=32 Hq=32 Hkv=8 D=128 page16 Skv=4096 over "
+                                     "4 GiB + 4 MiB caches, pages past byte 2^32 referenced"),
     "prefill_b4_s1024_int8": WorkloadSpec("prefill_b4_s1024_int8", "bf16", 4, 1024, 32, 8, 128,
                                           16, True, (0,), 11,
                                           "causal prefill, int8 K/V codes, bf16 q/out B=4 "
@@ -130,6 +140,9 @@ WORKLOADS = {
 }
 
 KV_KINDS = ("int8", "fp8_e4m3")
+
+# Pages per cache of ``decode_past_4gib``: 4 GiB + 4 MiB of 32 KiB pages.
+PAST_4GIB_PAGES = 131200
 
 WORKLOAD_ORDER = ["tiny_f32", "prefill_f16", "ragged_bf16", "llama3_8b_decode", "qwen3_235b_decode"]
 
@@ -157,6 +170,17 @@ class PagedInputs:
     @property
     def batch(self) -> int:
         return self.q.shape[0]
+
+
+def past_4gib_pages(gen, perm: torch.Tensor, total_used: int, page_bytes: int) -> torch.Tensor:
+    """``total_used`` distinct page ids in a seeded order: every page from the
+    one that ends at byte 2^32 to the last of the ``perm.numel()`` pages, the
+    rest taken from ``perm`` (a permutation of all ids) below that page."""
+    first_high = (1 << 32) // page_bytes - 1
+    high = torch.arange(first_high, perm.numel(), dtype=perm.dtype, device=perm.device)
+    low = perm[perm < first_high][: total_used - high.numel()]
+    both = torch.cat([high, low])
+    return both[torch.randperm(both.numel(), generator=gen, device=perm.device)]
 
 
 def _normal(gen, shape, dtype, device):
@@ -283,6 +307,10 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         b = batch if batch is not None else spec.batch
         lens = list(seq_lens) if seq_lens is not None else [8192] * b
         width, phys = 512, b * 512
+    elif name == "decode_past_4gib":
+        b = batch if batch is not None else spec.batch
+        lens = list(seq_lens) if seq_lens is not None else [4096] * b
+        width, phys = 256, PAST_4GIB_PAGES
     elif name in ("prefill_b4_s1024", "prefill_b1_s4096"):
         b = batch if batch is not None else spec.batch
         lens = list(seq_lens) if seq_lens is not None else [spec.seq_q] * b
@@ -304,6 +332,9 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
         perm = torch.arange(phys, dtype=torch.int64, device=device)
     else:
         perm = torch.randperm(phys, generator=gen, device=device)
+    if name == "decode_past_4gib":
+        page_bytes = ps * hkv * d * torch.empty((), dtype=dtype).element_size()
+        perm = past_4gib_pages(gen, perm, total_used, page_bytes)
     stride = width if table_stride is None else int(table_stride)
     if stride < width:
         raise ValueError("table stride smaller than its width")
@@ -321,7 +352,7 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
     q = _normal(gen, (bsz, spec.seq_q, hq, d), dtype, device)
     k_cache = _normal(gen, (phys, ps, hkv, d), dtype, device)
     v_cache = _normal(gen, (phys, ps, hkv, d), dtype, device)
-    if name in ("tiny_f32", "ragged_bf16", "prefill_f16"):
+    if name in ("tiny_f32", "ragged_bf16", "prefill_f16", "decode_past_4gib"):
         _poison_unused(k_cache, used, lens, table, ps)
         _poison_unused(v_cache, used, lens, table, ps)
 
@@ -340,7 +371,7 @@ def make_workload(name: str, device="cpu", seed: Optional[int] = None, variant: 
     inputs.notes["true_num_pages"] = phys
     inputs.notes["table_storage"] = storage
     inputs.notes["variant"] = variant
-    if variant == "straddle":
+    if variant == "straddle" or name == "decode_past_4gib":
         page_bytes = ps * hkv * d * k_cache.element_size()
         inputs.notes["max_used_page_start_bytes"] = int(used.max()) * page_bytes
     return inputs

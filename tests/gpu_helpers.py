@@ -2,12 +2,15 @@
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
 import torch
 
 import oracle.paged_attention as O
+from tolerance import assert_close
 
 
 def say(msg: str):
@@ -73,14 +76,49 @@ def oracle_splits(w, splits, causal=None):
                             w.scale, causal, splits)
 
 
-def oracle_sampled(w, batch_ids):
-    """Oracle (out, lse) for the sequences ``batch_ids`` of a large workload,
-    reading only the pages those sequences reference."""
+def oracle_workers() -> int:
+    """Threads for the oracle: the host cores this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def compare_every_sequence(w, out, lse, chunk=32, rows_per_task=128):
+    """Every output element and LSE of a large workload against the oracle.
+
+    Sequences are taken ``chunk`` at a time: the pages they reference are
+    copied to host (8-bit codes dequantized by the oracle), then the oracle
+    runs over every (sequence, block of ``rows_per_task`` query rows) on a
+    thread pool.  A causal block of rows starting at row ``i0`` is the oracle's
+    prefix-causal attention with offset ``L - Sq + i0``, which is bottom-right
+    causal masking for those rows.  Returns the largest |out error|."""
+    from threadpoolctl import threadpool_limits
+
+    out_h = out.float().cpu().numpy()
+    lse_h = lse.float().cpu().numpy()
+    q = host(w.q)
+    batch, seq_q = q.shape[0], q.shape[1]
     ps = w.k_cache.shape[1]
-    ids = referenced_pages(w.table_host, w.seq_lens_host, batch_ids, ps)
-    kp = HostPages(w.k_cache, ids, w.k_scale, w.kv)
-    vp = HostPages(w.v_cache, ids, w.v_scale, w.kv)
-    q = host(w.q[list(batch_ids)])
-    table = w.table_host[list(batch_ids)].numpy()
-    lens = np.array([w.seq_lens_host[b] for b in batch_ids])
-    return O.attention(q, kp, vp, table, lens, w.scale, w.causal)
+    worst = 0.0
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=oracle_workers()) as ex:
+        for c0 in range(0, batch, chunk):
+            ids = list(range(c0, min(c0 + chunk, batch)))
+            pages = referenced_pages(w.table_host, w.seq_lens_host, ids, ps)
+            kp = HostPages(w.k_cache, pages, w.k_scale, w.kv)
+            vp = HostPages(w.v_cache, pages, w.v_scale, w.kv)
+            tasks = [(b, i0, min(i0 + rows_per_task, seq_q)) for b in ids
+                     for i0 in range(0, seq_q, rows_per_task)]
+
+            def one(task):
+                b, i0, i1 = task
+                length = w.seq_lens_host[b]
+                prefix = [length - seq_q + i0] if w.causal else None
+                return O.attention(q[b:b + 1, i0:i1], kp, vp, w.table_host[b:b + 1].numpy(),
+                                   np.array([length]), w.scale, w.causal, prefix_offset=prefix)
+
+            for (b, i0, i1), (xo, xl) in zip(tasks, ex.map(one, tasks)):
+                err = assert_close(out_h[b, i0:i1], xo[0], w.q.dtype,
+                                   f"out, sequence {b} rows {i0}..{i1 - 1}")
+                assert_close(lse_h[b, i0:i1], xl[0], torch.float32,
+                             f"lse, sequence {b} rows {i0}..{i1 - 1}")
+                worst = max(worst, err)
+            del kp, vp
+    return worst

@@ -156,6 +156,60 @@ def test_split_resolution_prefill():
     assert pa.resolve_num_splits(s, 0) == 4
 
 
+def test_describe_plan():
+    """The planner query names the kernel family each shape takes (host only)."""
+    from paged_kv_cache_195_amd.api import PA_FP8_E4M3, PA_I8
+
+    def plan(s, splits=0):
+        return pa.describe_plan(s, splits)
+
+    # Llama-3-8B decode: one 16-row block per wave, 8 waves, 8 kv heads per workgroup, S = 1
+    p = plan(shape())
+    assert p == {"kernel": "mfma", "num_splits": 1, "rows_per_workgroup": 16, "row_groups": 1,
+                 "waves": 8, "kv_heads_per_workgroup": 8}
+    # Qwen3-235B decode (Hkv = 4): 4-wave workgroups
+    p = plan(shape(num_q_heads=64, num_kv_heads=4, max_pages_per_seq=512,
+                   block_table_stride=512))
+    assert (p["kernel"], p["waves"], p["kv_heads_per_workgroup"]) == ("mfma", 4, 4)
+    # 17..32 rows per kv head over >= 128 (sequence, kv head) pairs: two blocks per wave
+    for hq, hkv, batch in ((24, 1, 128), (256, 8, 16), (17, 1, 130)):
+        p = plan(shape(num_q_heads=hq, num_kv_heads=hkv, batch=batch))
+        assert (p["kernel"], p["rows_per_workgroup"], p["waves"]) == ("mfma_two_blocks", 32, 8)
+    # ... but not below 128 pairs (shared-tile kernel at D = 128)
+    assert plan(shape(num_q_heads=24, num_kv_heads=1, batch=127))["kernel"] == "shared_tile_teams"
+    # 16-bit D = 32 chunks of several queries take the two-block kernel (no shared-tile
+    # kernel at D = 32)
+    p = plan(shape(dtype=1, seq_q=6, num_q_heads=8, num_kv_heads=2, head_dim_qk=32,
+                   head_dim_v=32, batch=64))
+    assert p["kernel"] == "mfma_two_blocks"
+    # 8-bit caches: two blocks up to 63 rows, the shared-tile kernel (one team) from 64
+    assert plan(shape(kv_dtype=PA_I8, num_q_heads=48, num_kv_heads=1, batch=128))["kernel"] == \
+        "mfma_two_blocks"
+    p = plan(shape(kv_dtype=PA_FP8_E4M3, seq_q=16, batch=4, max_pages_per_seq=64,
+                   block_table_stride=64))
+    assert (p["kernel"], p["waves"], p["rows_per_workgroup"]) == ("shared_tile", 4, 128)
+    # prefill, 16-bit: D = 128 two teams, D = 64 one team
+    s = shape(batch=4, seq_q=1024, max_pages_per_seq=64, block_table_stride=64)
+    assert plan(s)["kernel"] == "shared_tile_teams"
+    s = shape(batch=4, seq_q=1024, head_dim_qk=64, head_dim_v=64, max_pages_per_seq=64,
+              block_table_stride=64)
+    assert plan(s)["kernel"] == "shared_tile"
+    # f32 caches: the vector-ALU kernel
+    assert plan(shape(dtype=0))["kernel"] == "valu"
+    # the split count agrees with pa_resolve_num_splits
+    for s in (shape(batch=8), shape(batch=1), shape(batch=8, max_pages_per_seq=63,
+                                                      block_table_stride=63)):
+        assert plan(s)["num_splits"] == pa.resolve_num_splits(s, 0)
+    assert plan(shape(), 7)["num_splits"] == 7
+    # errors
+    lib = pa.load_library()
+    assert lib.pa_describe_plan(ctypes.byref(shape()), 0, None) == PA_EINVAL
+    assert lib.pa_describe_plan(ctypes.byref(shape(batch=0)), 0,
+                                ctypes.byref(pa.api.PaPlanInfo())) == PA_EINVAL
+    assert lib.pa_describe_plan(ctypes.byref(shape()), -1,
+                                ctypes.byref(pa.api.PaPlanInfo())) == PA_EINVAL
+
+
 def test_combine_validation():
     lib = pa.load_library()
     assert lib.pa_combine(9, 4, 2, 128, FAKE, FAKE, FAKE, None, None) == PA_EINVAL

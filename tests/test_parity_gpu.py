@@ -1,9 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the f64 oracle.
 
 Small workloads are compared element by element in full (outputs, LSEs and,
-for split runs, the partials the workspace holds).  The two 2-GiB decode
-workloads run at full size in the bench's launch configuration and are
-compared on sampled sequences, plus properties that hold for every row.
+for split runs, the partials the workspace holds).  The full-size decode and
+prefill workloads run in the bench's launch configuration and are compared
+element by element in full as well (every sequence, head and query row).
 """
 
 import math
@@ -14,8 +14,7 @@ import torch
 
 import oracle.paged_attention as O
 import paged_kv_cache_195_amd as pa
-from gpu_helpers import (HostPages, host, oracle_full, oracle_sampled, oracle_splits,
-                         referenced_pages, say)
+from gpu_helpers import compare_every_sequence, host, oracle_full, oracle_splits, say
 from paged_kv_cache_195_amd.workloads import make_custom, make_workload
 from tolerance import assert_close
 
@@ -306,84 +305,73 @@ def test_combine_direct(dtype, rows, splits, dv, offset):
 
 
 # ----------------------------------------------------------------------------- full-size decode
-def _full_size(name, variant=None, sample=(0, 1, 77, 128, 200, 255)):
+def _need_free(gib):
     free, _ = torch.cuda.mem_get_info()
-    if free < 10 * 2 ** 30:
-        pytest.skip("needs about 10 GiB of free GPU memory")
+    if free < gib * 2 ** 30:
+        pytest.skip(f"needs about {gib} GiB of free GPU memory")
+
+
+def _full_batch(name, variant=None, chunk=32):
+    """A full-size workload in the bench's launch configuration (automatic
+    plan): every sequence, head and output element against the oracle."""
+    _need_free(12)
     w = make_workload(name, device=DEV, variant=variant)
     out, lse = run(w, 0)
-    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    # convex combination of V rows: |out| never exceeds the largest |v|
-    assert float(out.abs().max()) <= float(w.v_cache.abs().max())
-    batch_ids = list(sample)
-    if variant == "straddle":
-        # include sequences whose pages sit past byte 2^31 (and below it)
-        page_bytes = w.k_cache[0].numel() * w.k_cache.element_size()
-        hi = (w.table_host.long() * page_bytes >= 2 ** 31).any(dim=1).nonzero().flatten().tolist()
-        lo = (w.table_host.long() * page_bytes < 2 ** 31).all(dim=1).nonzero().flatten().tolist()
-        batch_ids = sorted(set(hi[:4] + lo[:2] + batch_ids[:2]))
-        assert hi, "no sequence references a page past 2^31 bytes"
-    xo, xl = oracle_sampled(w, batch_ids)
-    assert_close(out[batch_ids], xo, torch.bfloat16, "out")
-    assert_close(lse[batch_ids], xl, torch.float32, "lse")
-    return w, batch_ids
-
-
-def test_llama3_8b_decode_full_size_sampled():
-    say("llama3_8b_decode full size, sampled parity")
-    _full_size("llama3_8b_decode")
+    worst = compare_every_sequence(w, out, lse, chunk=chunk)
+    say(f"{name} {variant or ''}: all {w.batch} sequences within tolerance, "
+        f"max |out err| {worst:.2e}")
+    return w
 
 
 def test_llama3_8b_decode_full_batch():
-    """The metric's workload, every one of its 256 sequences against the oracle
-    (pages copied to host 32 sequences at a time, the oracle run on 8 threads)."""
-    import concurrent.futures as cf
-
-    from threadpoolctl import threadpool_limits
-
+    """The metric's workload, every one of its 256 sequences against the oracle."""
     say("llama3_8b_decode full size, all 256 sequences against the oracle")
-    free, _ = torch.cuda.mem_get_info()
-    if free < 10 * 2 ** 30:
-        pytest.skip("needs about 10 GiB of free GPU memory")
-    w = make_workload("llama3_8b_decode", device=DEV)
-    out, lse = run(w, 0)
-    out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
-    q = host(w.q)
-    ps = w.k_cache.shape[1]
-    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=8) as ex:
-        for c0 in range(0, w.batch, 32):
-            ids = list(range(c0, min(c0 + 32, w.batch)))
-            pages = referenced_pages(w.table_host, w.seq_lens_host, ids, ps)
-            kp, vp = HostPages(w.k_cache, pages), HostPages(w.v_cache, pages)
-
-            def one(b):
-                return O.attention(q[b:b + 1], kp, vp, w.table_host[b:b + 1].numpy(),
-                                   np.array([w.seq_lens_host[b]]), w.scale, False)
-
-            for b, (xo, xl) in zip(ids, ex.map(one, ids)):
-                assert_close(out_h[b], xo[0], torch.bfloat16, f"out, sequence {b}")
-                assert_close(lse_h[b], xl[0], torch.float32, f"lse, sequence {b}")
+    _full_batch("llama3_8b_decode")
 
 
-def test_qwen3_235b_decode_full_size_sampled():
-    say("qwen3_235b_decode full size, sampled parity")
-    _full_size("qwen3_235b_decode")
+def test_qwen3_235b_decode_full_batch():
+    say("qwen3_235b_decode full size, all 256 sequences against the oracle")
+    _full_batch("qwen3_235b_decode")
 
 
-def test_llama3_70b_decode_full_size_sampled():
-    say("llama3_70b_decode full size (G=8), sampled parity")
-    _full_size("llama3_70b_decode")
-
-
-def test_decode_b64_s8192_g8_full_size_sampled():
-    say("decode_b64_s8192_g8 full size (G=8), sampled parity")
-    _full_size("decode_b64_s8192_g8", sample=(0, 17, 40, 63))
-
-
-def test_qwen3_235b_decode_straddles_2gib():
-    say("qwen3_235b_decode straddle variant (pages past 2^31 bytes)")
-    w, ids = _full_size("qwen3_235b_decode", variant="straddle")
+def test_qwen3_235b_decode_straddles_2gib_full_batch():
+    """Caches of 2 GiB + 4 MiB whose referenced pages lie on both sides of byte
+    2^31: every sequence against the oracle."""
+    say("qwen3_235b_decode straddle variant (pages past 2^31 bytes), all 256 sequences")
+    w = _full_batch("qwen3_235b_decode", variant="straddle")
     assert w.notes["max_used_page_start_bytes"] >= 2 ** 31
+    page_bytes = w.k_cache[0].numel() * w.k_cache.element_size()
+    starts = w.table_host.long() * page_bytes
+    assert bool((starts >= 2 ** 31).any()) and bool((starts < 2 ** 31).any())
+
+
+def test_llama3_70b_decode_full_batch():
+    say("llama3_70b_decode full size (G=8), all 256 sequences against the oracle")
+    _full_batch("llama3_70b_decode")
+
+
+def test_decode_b64_s8192_g8_full_batch():
+    say("decode_b64_s8192_g8 full size (G=8), all 64 sequences against the oracle")
+    _full_batch("decode_b64_s8192_g8")
+
+
+def test_decode_past_4gib_full_batch():
+    """K and V caches of 4 GiB + 4 MiB each, every page from the one ending at
+    byte 2^32 to the last referenced, unreferenced pages NaN: a page base formed
+    in 32 bits (or sign-extended) would read the wrong page or a NaN one.
+    Every sequence against the oracle."""
+    _need_free(24)
+    say("decode_past_4gib: 4 GiB + 4 MiB caches, pages at and past byte 2^32, all sequences")
+    w = make_workload("decode_past_4gib", device=DEV)
+    page_bytes = w.k_cache[0].numel() * w.k_cache.element_size()
+    assert w.k_cache.numel() * w.k_cache.element_size() > 2 ** 32
+    starts = w.table_host.long() * page_bytes
+    assert int((starts >= 2 ** 32).sum()) == 128
+    for splits in (0, 3):
+        out, lse = run(w, splits)
+        worst = compare_every_sequence(w, out, lse)
+        say(f"decode_past_4gib S={splits}: all {w.batch} sequences within tolerance, "
+            f"max |out err| {worst:.2e}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
@@ -401,39 +389,24 @@ def test_scale_values(scale):
         assert_close(lse, xl, torch.float32, f"lse S={splits}")
 
 
-def _prefill_full_size(name, rows=(0, 1, 15, 16, 255, 511, 512, 1023)):
-    """Full-size causal prefill; sampled rows checked one by one: row i of a causal
-    prefill over L keys attends to the first L - Sq + i + 1 keys, which is the
-    oracle's decode over that shorter sequence."""
+def _prefill_full_size(name):
+    """Full-size causal prefill in the bench's launch configuration: every row
+    of every sequence against the oracle (blocks of rows as prefix-causal
+    attention at their own offsets)."""
     w = make_workload(name, device=DEV)
     out, lse = run(w, 0)
-    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    sq = w.q.shape[1]
-    picks = [i for i in rows if i < sq] + [sq - 1]
-    ps = w.k_cache.shape[1]
-    for b in range(w.q.shape[0]):
-        length = w.seq_lens_host[b]
-        n = -(-length // ps)
-        pages = w.table_host[b, :n].tolist()
-        kp = HostPages(w.k_cache, pages)
-        vp = HostPages(w.v_cache, pages)
-        for i in picks:
-            visible = length - sq + i + 1
-            xo, xl = O.attention(host(w.q[b:b + 1, i:i + 1]), kp, vp,
-                                 w.table_host[b:b + 1].numpy(), np.array([visible]), w.scale,
-                                 False)
-            assert_close(out[b, i], xo[0, 0], torch.bfloat16, f"out b={b} i={i}")
-            assert_close(lse[b, i], xl[0, 0], torch.float32, f"lse b={b} i={i}")
+    worst = compare_every_sequence(w, out, lse, chunk=1)
+    say(f"{name}: every row within tolerance, max |out err| {worst:.2e}")
 
 
-def test_prefill_b4_s1024_full_size_sampled():
-    say("prefill_b4_s1024 full size, sampled rows")
+def test_prefill_b4_s1024_full_size():
+    say("prefill_b4_s1024 full size, every row")
     _prefill_full_size("prefill_b4_s1024")
 
 
-def test_prefill_b1_s4096_full_size_sampled():
-    say("prefill_b1_s4096 full size, sampled rows")
-    _prefill_full_size("prefill_b1_s4096", rows=(0, 7, 100, 1000, 2047, 2048, 4000))
+def test_prefill_b1_s4096_full_size():
+    say("prefill_b1_s4096 full size, every row")
+    _prefill_full_size("prefill_b1_s4096")
 
 
 @pytest.mark.parametrize("dtype,d,ps,hq,hkv,seq_q,lens,causal,splits", [

@@ -1,8 +1,10 @@
 """The matrix-core kernel with two 16-row blocks per wave (17 to 32 query rows
 per kv head share each staged K/V tile), used over batches of at least 128
-(sequence, kv head) pairs: decode at group sizes 17..32, and 8-bit caches with
-17 to 63 rows; plus a small 8-bit batch that keeps one block per wave.  Against
-the f64 oracle, with the split partials for S > 1."""
+(sequence, kv head) pairs: decode at group sizes 17..32, 16-bit chunks of
+several queries at D = 32, and 8-bit caches with 17 to 63 rows; plus a small
+8-bit batch that keeps one block per wave; prefix offsets and the page-id
+range check on this kernel.  Against the f64 oracle, with the split partials
+for S > 1.  Each case first asks the planner which kernel it takes."""
 
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ DEV = "cuda"
 
 # (q dtype, kv codes, D, page, Hq, Hkv, batch, Sq)
 CASES = [
-    ("bf16", None, 128, 16, 24, 1, 128, 1),          # G = 24, 4-wave workgroups
+    ("bf16", None, 128, 16, 24, 1, 128, 1),          # G = 24, one kv head per workgroup
     ("f16", None, 64, 32, 160, 8, 16, 1),            # G = 20, 8-wave workgroups
     ("bf16", None, 128, 16, 256, 8, 16, 1),          # G = 32: one full row group
     ("bf16", None, 32, 16, 17, 1, 130, 1),           # G = 17, D = 32
@@ -27,6 +29,7 @@ CASES = [
     ("f16", "fp8_e4m3", 64, 16, 80, 2, 64, 1),       # 8-bit, G = 40: two row groups of 32
     ("bf16", "int8", 128, 16, 32, 8, 16, 6),         # 8-bit chunk of 6 queries: 24 rows
     ("bf16", "int8", 128, 16, 48, 2, 4, 1),          # small batch: one row block per wave
+    ("f16", None, 32, 16, 8, 2, 64, 6),              # 16-bit D = 32 causal chunk: 24 rows
 ]
 
 
@@ -44,6 +47,8 @@ def test_two_row_blocks_per_wave(case, splits):
                     kv=kv)
     shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
     s = pa.resolve_num_splits(shape, splits)
+    want = "mfma" if batch * hkv < 128 else "mfma_two_blocks"
+    assert pa.describe_plan(shape, splits)["kernel"] == want
     fn = pa.decode if sq == 1 else pa.prefill
     out, lse, ws = fn(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
                       causal=causal, num_splits=splits, num_pages=w.num_pages_arg,
@@ -60,3 +65,83 @@ def test_two_row_blocks_per_wave(case, splits):
         xo, xl = O.split_partials(*args, s)
         assert_close(po, xo.reshape(rows, s, -1), w.q.dtype, "part_out")
         assert_close(pl, xl.reshape(rows, s), w.q.dtype, "part_lse")
+
+
+# (q dtype, kv codes, D, page, Hq, Hkv, batch, Sq): shapes on the two-block kernel
+OPTION_CASES = [
+    ("bf16", None, 128, 16, 24, 1, 128, 1),
+    ("f16", None, 32, 32, 8, 2, 64, 6),
+    ("bf16", "int8", 128, 16, 48, 2, 64, 1),
+    ("f16", "fp8_e4m3", 64, 16, 64, 8, 16, 3),
+]
+
+
+def _two_block_workload(case, seed, extra_pages=5):
+    dtype, kv, d, ps, hq, hkv, batch, sq = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 201, size=batch).tolist()
+    lens[0], lens[-1] = 200, 0
+    w = make_custom(dtype, lens, hq, hkv, d, ps, seq_q=sq, causal=sq > 1, width=14,
+                    extra_pages=extra_pages, seed=seed, device=DEV, kv=kv)
+    shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
+    assert pa.describe_plan(shape, 0)["kernel"] == "mfma_two_blocks"
+    return w, lens
+
+
+@pytest.mark.parametrize("case", OPTION_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}-D{c[2]}-G{c[4] // c[5]}-B{c[6]}-Sq{c[7]}")
+@pytest.mark.parametrize("splits", [1, 3])
+def test_two_block_prefix_offset(case, splits):
+    """Prefix offsets (before the first key, inside, at the end and past it)
+    on the two-block kernel."""
+    w, lens = _two_block_workload(case, 81)
+    rng = np.random.default_rng(82)
+    prefix = [int(rng.integers(-10, x + 10)) for x in lens]
+    prefix[1] = -1
+    say(f"two row blocks + prefix offsets: {case} S={splits}")
+    po = torch.tensor(prefix, dtype=torch.int32, device=DEV)
+    fn = pa.decode if w.q.shape[1] == 1 else pa.prefill
+    out, lse, ws = fn(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
+                      num_splits=splits, num_pages=w.num_pages_arg, return_workspace=True,
+                      prefix_offset=po, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    k, v = host_caches(w)
+    args = (host(w.q), k, v, w.table_host.numpy(), np.array(lens), w.scale, False)
+    xo, xl = O.attention(*args, prefix_offset=prefix)
+    assert_close(out, xo, w.q.dtype, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+    if splits > 1:
+        rows = w.q.shape[0] * w.q.shape[1] * w.q.shape[2]
+        po_, pl_ = pa.split_views(ws, rows, splits, w.v_cache.shape[3])
+        xo, xl = O.split_partials(*args, splits, prefix_offset=prefix)
+        assert_close(po_, xo.reshape(rows, splits, -1), w.q.dtype, "part_out")
+        assert_close(pl_, xl.reshape(rows, splits), w.q.dtype, "part_lse")
+
+
+@pytest.mark.parametrize("case", OPTION_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}-D{c[2]}-G{c[4] // c[5]}-B{c[6]}-Sq{c[7]}")
+@pytest.mark.parametrize("splits", [1, 3])
+def test_two_block_page_check(case, splits):
+    """The page-id range check ahead of the two-block kernel: a stated page
+    count below the cache's fails the sequences holding larger ids (still
+    allocated memory, so a slip shows as a wrong value, not a fault)."""
+    w, lens = _two_block_workload(case, 83, extra_pages=0)
+    table = w.table_host.numpy()
+    ps = w.k_cache.shape[1]
+    top = sorted(max(table[b, : -(-x // ps)]) for b, x in enumerate(lens) if x > 0)
+    stated = int(top[len(top) // 2])
+    first_bad, att = O.check_pages(table, lens, ps, stated, table.shape[1])
+    assert 0 <= first_bad and 0 < sum(a != x for a, x in zip(att, lens)) < len(lens)
+    say(f"two row blocks + page check: {case} stated {stated} S={splits}")
+    res = torch.zeros(len(lens) + 1, dtype=torch.int32, device=DEV)
+    fn = pa.decode if w.q.shape[1] == 1 else pa.prefill
+    causal = w.q.shape[1] > 1
+    out, lse = fn(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale, causal=causal,
+                  num_splits=splits, num_pages=stated, page_check=res, k_scale=w.k_scale,
+                  v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    assert res.tolist() == [first_bad] + att
+    k, v = host_caches(w)
+    xo, xl = O.attention(host(w.q), k, v, table, np.array(att), w.scale, causal)
+    assert_close(out, xo, w.q.dtype, "out")
+    assert_close(lse, xl, torch.float32, "lse")

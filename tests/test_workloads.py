@@ -96,3 +96,25 @@ def test_missing_library_raises():
             api.load_library("/nonexistent/libpa.so")
     finally:
         api._lib = saved
+
+
+def test_past_4gib_page_selection():
+    """The 4 GiB + 4 MiB decode workload references every page that starts at
+    or past byte 2^32 and the page that ends there; the rest lie below, all
+    distinct, in a seeded shuffled order."""
+    from paged_kv_cache_195_amd.workloads import PAST_4GIB_PAGES, past_4gib_pages
+
+    page_bytes = 16 * 8 * 128 * 2
+    gen = torch.Generator().manual_seed(13)
+    perm = torch.randperm(PAST_4GIB_PAGES, generator=gen)
+    ids = past_4gib_pages(gen, perm, 32 * 256, page_bytes)
+    assert ids.numel() == 8192 and len(set(ids.tolist())) == 8192
+    starts = ids * page_bytes
+    assert int((starts >= 2 ** 32).sum()) == 128          # ids 131072..131199
+    assert int(ids.max()) == PAST_4GIB_PAGES - 1
+    assert (131071 in ids.tolist()) and 131071 * page_bytes + page_bytes == 2 ** 32
+    assert PAST_4GIB_PAGES * page_bytes == 2 ** 32 + 4 * 2 ** 20
+    # spread over the table: most 256-page rows hold at least one page past 2^32
+    rows = ids.view(32, 256)
+    assert int(((rows * page_bytes) >= 2 ** 32).any(dim=1).sum()) >= 24
+    assert ids.tolist() != sorted(ids.tolist())
