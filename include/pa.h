@@ -23,6 +23,8 @@
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE memory owned by the caller.  The library
  *    allocates nothing and keeps no state between calls; it is thread-safe.
+ *    (pa_decode_noalloc is the exception: it keeps its split partials in one
+ *    static device array per GPU, shared by its calls on that GPU.)
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and the call returns without waiting for it.
  *  - Every argument check runs on the host before anything is launched.  A
@@ -80,7 +82,9 @@ typedef enum pa_status {
                            num_splits out of range, seq_q != 1 in pa_decode   */
   PA_EUNSUPPORTED = -2, /* valid but outside the compiled envelope            */
   PA_EWORKSPACE = -3,   /* workspace NULL or smaller than pa_workspace_bytes  */
-  PA_EHIP = -4          /* the HIP runtime refused a launch                   */
+  PA_EHIP = -4,         /* the HIP runtime refused a launch                   */
+  PA_ESCRATCH = -5      /* pa_decode_noalloc: the split partials need more than
+                           PA_NOALLOC_SCRATCH_BYTES                            */
 } pa_status;
 
 /* Problem shape shared by pa_decode, pa_prefill and pa_workspace_bytes. */
@@ -277,6 +281,36 @@ size_t pa_workspace_bytes(const pa_shape* shape, int num_splits);
  * on device data), so it is known on the host without a synchronisation.
  * Negative pa_status for an invalid shape or num_splits. */
 int pa_resolve_num_splits(const pa_shape* shape, int num_splits);
+
+/*
+ * pa_decode_noalloc -- pa_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  It takes no workspace.  The split-KV partials (the only
+ * scratch the path uses, S > 1) go to a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine); on its first call on
+ * a device it looks up that device's copy of the array.
+ *
+ *  options     as for pa_decode_ex, or NULL (then it is pa_decode).
+ *  All other arguments, results and checks as for pa_decode_ex.  The device
+ *  is the current one, which must be the device of `stream` and the tensors.
+ *
+ * Returns PA_ESCRATCH, before anything is launched, when the resolved split
+ * count needs more partials than the array holds (pa_workspace_bytes(shape,
+ * num_splits) > PA_NOALLOC_SCRATCH_BYTES; e.g. B * Hq * S * (Dv + 1) * 4
+ * bytes at Sq = 1, so B = 256, Hq = 32, Dv = 128 allows S <= 3).  Calls on
+ * one GPU share its array: calls that overlap in time on that GPU (on
+ * different streams, or from several threads without ordering) race and may
+ * return wrong results.  Calls ordered on one stream are safe; each call
+ * writes every partial it later reads, so nothing has to be cleared between
+ * calls.  The partials are not exposed.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int pa_decode_noalloc(const pa_shape* shape, const pa_options* options, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float scale, int causal, int num_splits,
+                      void* out, float* lse, void* stream);
 
 /* Kernel families a call can take (pa_plan_info.kernel). */
 typedef enum pa_kernel {

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     PaShape,
     combine,
     decode,
+    decode_noalloc,
     describe_plan,
     load_library,
     make_shape,

@@ -18,14 +18,17 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_I8, PA_FP8_E4M3 = 0, 1, 2, 3, 4
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ESCRATCH = 0, -1, -2, -3, -4, -5
+# bytes of the static partials array pa_decode_noalloc uses (PA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 # 8-bit cache codes (pa_shape.kv_dtype)
 KV_CODE = {torch.int8: PA_I8, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 # The functions include/pa.h declares.
-EXPORTS = ("pa_decode", "pa_prefill", "pa_decode_ex", "pa_prefill_ex", "pa_combine",
-           "pa_workspace_bytes", "pa_resolve_num_splits", "pa_describe_plan", "pa_strerror")
+EXPORTS = ("pa_decode", "pa_prefill", "pa_decode_ex", "pa_prefill_ex", "pa_decode_noalloc",
+           "pa_combine", "pa_workspace_bytes", "pa_resolve_num_splits", "pa_describe_plan",
+           "pa_strerror")
 # pa_kernel
 KERNEL_NAMES = {0: "valu", 1: "mfma", 2: "mfma_two_blocks", 3: "shared_tile",
                 4: "shared_tile_teams"}
@@ -100,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_ex.restype = ctypes.c_int
     lib.pa_prefill_ex.argtypes = ex_args
     lib.pa_prefill_ex.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = ex_args[:-3] + [vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.pa_combine.restype = ctypes.c_int
     lib.pa_workspace_bytes.argtypes = [shape_p, ctypes.c_int]
@@ -263,6 +268,48 @@ def prefill(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bo
     return _attention("pa_prefill", q, k_cache, v_cache, block_table, seq_lens, scale, causal,
                       num_splits, out, lse, num_pages, workspace, return_workspace,
                       prefix_offset, page_check, k_scale, v_scale)
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, scale: float,
+                   causal: bool = False, num_splits: int = 0, out=None, lse=None,
+                   num_pages: Optional[int] = None, prefix_offset=None, page_check=None,
+                   k_scale=None, v_scale=None):
+    """Paged decode through ``pa_decode_noalloc``: no workspace, the split
+    partials go to the library's static device array.  ``q`` is ``[B, 1, Hq,
+    D]``; pass ``out`` ([B, 1, Hq, Dv], q's dtype) and ``lse`` ([B, 1, Hq]
+    float32) to keep the call free of allocations (else they are allocated
+    here, outside the library).  Returns ``(out, lse)``."""
+    lib = _current()
+    _validate_tensors(q, k_cache, v_cache, block_table, seq_lens)
+    shape = make_shape(q, k_cache, v_cache, block_table, num_pages)
+    batch, seq_q, hq, _ = q.shape
+    dv = v_cache.shape[3]
+    _int32_vector("prefix_offset", prefix_offset, batch)
+    _int32_vector("page_check", page_check, batch + 1)
+    if shape.kv_dtype:
+        _scales("k_scale", k_scale, k_cache)
+        _scales("v_scale", v_scale, k_cache)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("scales are for 8-bit caches only")
+    if out is None:
+        out = torch.empty((batch, seq_q, hq, dv), dtype=q.dtype, device=q.device)
+    elif not out.is_contiguous() or out.dtype != q.dtype or out.numel() != batch * seq_q * hq * dv:
+        raise ValueError("out must be a contiguous [B, Sq, Hq, Dv] tensor of q's dtype")
+    if lse is None:
+        lse = torch.empty((batch, seq_q, hq), dtype=torch.float32, device=q.device)
+    elif not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != batch * seq_q * hq:
+        raise ValueError("lse must be a contiguous float32 [B, Sq, Hq] tensor")
+    opts = PaOptions(prefix_offset=None if prefix_offset is None else prefix_offset.data_ptr(),
+                     page_check=None if page_check is None else page_check.data_ptr(),
+                     k_scale=None if k_scale is None else k_scale.data_ptr(),
+                     v_scale=None if v_scale is None else v_scale.data_ptr())
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = lib.pa_decode_noalloc(ctypes.byref(shape), ctypes.byref(opts), _ptr(q),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(seq_lens), ctypes.c_float(scale), int(bool(causal)),
+                                   int(num_splits), _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    _check(status, "pa_decode_noalloc")
+    return out, lse
 
 
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, dtype: torch.dtype,

@@ -32,6 +32,7 @@ SOURCES = [
     "attn_mfma_q_bf16.hip",
     "combine.hip",
     "page_check.hip",
+    "pa_noalloc.hip",
 ]
 
 COMMON_FLAGS = [

@@ -183,6 +183,10 @@ int check_splits(int num_splits) {
   return (num_splits < 0 || num_splits > kMaxSplits) ? PA_EINVAL : PA_OK;
 }
 
+}  // namespace
+
+namespace pa {
+
 int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const void* q,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
@@ -274,7 +278,7 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
   return PA_OK;
 }
 
-}  // namespace
+}  // namespace pa
 
 extern "C" {
 
@@ -282,7 +286,7 @@ int pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const v
               const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
               int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
               void* stream) {
-  return run_attention(shape, nullptr, true, q, k_cache, v_cache, block_table, seq_lens, scale,
+  return pa::run_attention(shape, nullptr, true, q, k_cache, v_cache, block_table, seq_lens, scale,
                        causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -290,7 +294,7 @@ int pa_prefill(const pa_shape* shape, const void* q, const void* k_cache, const 
                const int32_t* block_table, const int32_t* seq_lens, float scale, int causal,
                int num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
                void* stream) {
-  return run_attention(shape, nullptr, false, q, k_cache, v_cache, block_table, seq_lens, scale,
+  return pa::run_attention(shape, nullptr, false, q, k_cache, v_cache, block_table, seq_lens, scale,
                        causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -298,7 +302,7 @@ int pa_decode_ex(const pa_shape* shape, const pa_options* options, const void* q
                  const void* k_cache, const void* v_cache, const int32_t* block_table,
                  const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_attention(shape, options, true, q, k_cache, v_cache, block_table, seq_lens, scale,
+  return pa::run_attention(shape, options, true, q, k_cache, v_cache, block_table, seq_lens, scale,
                        causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -306,7 +310,7 @@ int pa_prefill_ex(const pa_shape* shape, const pa_options* options, const void* 
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_attention(shape, options, false, q, k_cache, v_cache, block_table, seq_lens, scale,
+  return pa::run_attention(shape, options, false, q, k_cache, v_cache, block_table, seq_lens, scale,
                        causal, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -367,6 +371,8 @@ const char* pa_strerror(int status) {
     case PA_EUNSUPPORTED: return "shape or dtype outside the compiled envelope";
     case PA_EWORKSPACE: return "workspace missing or too small";
     case PA_EHIP: return "HIP runtime error at launch";
+    case PA_ESCRATCH:
+      return "split partials larger than the library's static scratch (PA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -3,7 +3,10 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "pa.h"
 
 namespace pa {
 
@@ -134,6 +137,14 @@ hipError_t launch_attn_mfma_q_f16(const AttnParams& p, const AttnPlan& plan, int
                                   int head_dim, int page_size, int batch, hipStream_t stream);
 hipError_t launch_attn_mfma_q_bf16(const AttnParams& p, const AttnPlan& plan, int kv_dtype,
                                    int head_dim, int page_size, int batch, hipStream_t stream);
+
+// Validation, planning and launches of one pa_decode / pa_prefill call (with
+// the optional inputs of pa_options, which may be null); the split partials go
+// to `workspace`.  Returns a pa_status.
+int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, float scale, int causal, int num_splits, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 hipError_t launch_combine(int dtype, int rows, int num_splits, int head_dim_v,
                           const float* part_out, const float* part_lse, void* out, float* lse,

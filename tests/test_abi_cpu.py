@@ -228,8 +228,29 @@ def test_combine_validation():
 
 
 def test_strerror():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert pa.strerror(code) and pa.strerror(code) != pa.strerror(99)
+
+
+def test_noalloc_host_checks():
+    """pa_decode_noalloc rejects, on the host and before any HIP call, split
+    partials past its static array (PA_ESCRATCH) and invalid shapes."""
+    from paged_kv_cache_195_amd.api import NOALLOC_SCRATCH_BYTES, PA_ESCRATCH
+
+    lib = pa.load_library()
+
+    def call(s, splits):
+        return lib.pa_decode_noalloc(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     ctypes.c_float(0.1), 0, splits, FAKE, None, None)
+
+    s = shape()   # B=256, Hq=32, Dv=128: S=3 fits 16 MiB, S=4 does not
+    assert pa.workspace_bytes(s, 3) <= NOALLOC_SCRATCH_BYTES < pa.workspace_bytes(s, 4)
+    assert call(s, 4) == PA_ESCRATCH and call(s, 200) == PA_ESCRATCH
+    assert call(shape(batch=0), 0) == PA_EINVAL
+    assert call(shape(seq_q=2), 0) == PA_EINVAL          # decode needs Sq == 1
+    assert call(shape(), -1) == PA_EINVAL
+    assert call(shape(), 300) == PA_EINVAL               # past the 256-split limit
+    assert call(shape(head_dim_qk=96, head_dim_v=96), 0) == PA_EUNSUPPORTED
 
 
 def test_binding_rejects_cpu_tensors():
