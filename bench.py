@@ -168,7 +168,8 @@ def cpu_baseline(w, out_gpu, budget_s: float, threads: int):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{len(done)} of {batch} sequences (whole sequences, all heads), f64 NumPy, "
-                  f"{threads} threads x 1 BLAS thread, {elapsed:.1f} s wall",
+                  f"{threads} threads x 1 BLAS thread on {len(os.sched_getaffinity(0))} visible "
+                  f"host cores, {elapsed:.1f} s wall",
         "max_abs_err_vs_gpu": max_err,
         "parity": {"ok": n_bad == 0, "elements_out_of_tolerance": n_bad,
                    "atol": atol, "rtol": rtol},
@@ -215,6 +216,9 @@ def main():
     ap.add_argument("--variant", default=None,
                     help="'contiguous' for an identity page order; 'straddle' (qwen3 only) for "
                          "a 2 GiB + 4 MiB cache")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="keys per sequence for every sequence of a decode workload (default: "
+                         "the workload's own; for counter runs at several lengths)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -237,7 +241,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
         return
-    w = make_workload(args.workload, device="cuda", variant=args.variant)
+    lens = None
+    if args.seq_len is not None:
+        from paged_kv_cache_195_amd.workloads import WORKLOADS
+        lens = [args.seq_len] * WORKLOADS[args.workload].batch
+    w = make_workload(args.workload, device="cuda", variant=args.variant, seq_lens=lens)
     shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
     splits = pa.resolve_num_splits(shape, args.splits)
     ws_bytes = pa.workspace_bytes(shape, args.splits)
@@ -352,14 +360,21 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(spec.name) if (splits == 1 and not args.variant) else None,
+            "traffic": (measured_traffic(spec.name)
+                        if (splits == 1 and not args.variant and args.seq_len is None) else None),
         },
     }
     if splits > 1:
         line["roofline"]["note"] = "step = attention + combine kernels"
     if not args.no_cpu_baseline:
-        threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-        line["cpu_baseline"] = cpu_baseline(w, out[:, 0], args.cpu_budget, threads)
+        # at most 16 threads: the host CPU share of one GPU on the measuring box,
+        # whatever count of cores the process is allowed to see
+        visible = len(os.sched_getaffinity(0))
+        threads = max(1, min(visible, 16))
+        base = cpu_baseline(w, out[:, 0], args.cpu_budget, threads)
+        base["host_cores_visible"] = visible
+        base["gpu_over_oracle"] = round(gbps / base["value"], 1) if base["value"] > 0 else None
+        line["cpu_baseline"] = base
     print(json.dumps(line), flush=True)
     if "cpu_baseline" in line and not line["cpu_baseline"]["parity"]["ok"]:
         print("bench.py: the GPU output of the timed workload disagrees with the oracle",
