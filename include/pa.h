@@ -119,13 +119,9 @@ typedef struct pa_shape {
  * LSE and split partials within 1e-5 + 1e-5 |x| (partials of 16-bit problems
  * within the 16-bit bound).  Scores and the softmax run in float32; 16-bit
  * problems multiply on the matrix cores with the softmax weights kept to at
- * least 11 significant bits.  With 8-bit caches and 64 or more query rows
- * per kv head (the shared-tile prefill kernel), each page's V scale joins the
- * f16 weights relative to the largest |V scale| met so far: the bound above
- * is met while the V scales of the pages a row reads lie within 2^6 of each
- * other; pages whose V scales are far below the largest keep less relative
- * precision in their (small) share of the output.  Results are
- * deterministic: the same inputs give the same bits on every call.
+ * least 11 significant bits, for 8-bit caches whatever the spread of their
+ * K and V scales.  Results are deterministic: the same inputs give the same
+ * bits on every call.
  */
 
 /*

@@ -61,8 +61,21 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
                         __builtin_bit_cast(float, w & 0xffff0000u));
 }
 
-template <typename T, int D, int PS, int NW, int RB, typename KV = KvSame>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const AttnParams p) {
+typedef __attribute__((address_space(3))) float lds_float;
+
+// LDS of the kernel: two K/V tile buffers of 64 rows.
+template <int D>
+constexpr int prefill_tile_lds() {
+  return 2 * 2 * 64 * D * 2;
+}
+
+// The whole computation of one workgroup.  kExact (8-bit codes only) adds the
+// per-tile test for V factors far below the running reference.  Without it,
+// a workgroup whose pages' V scales lie more than 2^6 apart returns false
+// before any tile is read, and the kernel runs it again with kExact.
+template <typename T, int D, int PS, int NW, int RB, typename KV, bool kExact>
+__device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem3,
+                                             lds_float* sub_scale) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(PS == 16 || PS == 32, "page size");
   // 8-bit K/V codes (KvI8, KvFp8): both tiles pass through registers and are
@@ -73,10 +86,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   // the largest |V scale| the wave has met (the accumulators are rescaled when
   // it grows, like the running max), so a weight never exceeds its unscaled
   // value and no scale overflows f16; the output is multiplied by vref at the
-  // end.  The weights keep f16's relative precision while vs / vref times the
-  // weight stays a normal f16 number: V scales within 2^6 of each other keep
-  // every weight down to 2^-8 exact to 2^-12; pages whose V scales are far
-  // below the largest lose relative precision in their (small) share.
+  // end.  While every sub-tile of a tile has |vs / vref| >= 2^-6, its weights
+  // down to 2^-8 stay normal f16 numbers, exact to 2^-12.  A tile holding a
+  // sub-tile further below (a wave-uniform test on the scales) adds that
+  // sub-tile on its own: with vs / vref = m 2^E (|m| in [1, 2)), O is scaled
+  // by 2^-E, takes the sub-tile's P . V with its weights times m, and is
+  // scaled back by 2^E (exact in f32) -- so the weights keep f16's relative
+  // precision however far apart the V scales lie.
   constexpr bool kQuant = KvTraits<KV>::quant;
   constexpr int kTile = 64;                      // tokens per tile
   constexpr int kSub = kTile / 16;               // 16-token sub-tiles
@@ -92,6 +108,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   constexpr int kRowsPerWaveQ = 16 * RB;         // query rows per wave
   constexpr int kBuf = kTile * kRowBytes;        // one K or V tile in LDS
   constexpr float kSlack = 8.f;
+  constexpr float kFarScale = 1.f / 64.f;  // 8-bit codes: V factors below this take half_pv_sub
   constexpr bool kConvertV = !kQuant && std::is_same<T, bf16_t>::value;  // bf16 V goes to f16
   constexpr int kCacheRowBytes = kQuant ? D : kRowBytes;  // a K or V row in the cache
   constexpr int kCodeChunks = D / 16;                     // 16-byte chunks of a code row
@@ -200,11 +217,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kCacheRowBytes;
   pt.n_pages = n_pages;
 
-  // ---- LDS: two K/V tile buffers (swizzled rows); for 8-bit codes also the
-  // K and V scales of each buffer's 16-token sub-tiles
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kBuf];
-  __shared__ float sub_scale[kQuant ? 2 * 2 * kSub : 1];  // [buf][K, V][sub-tile]
-  lds_char* smem3 = (lds_char*)(smem);
+  if constexpr (kQuant && !kExact) {
+    // The largest and the smallest nonzero |V scale| of the split's pages
+    // (this kv head): only when they lie more than 2^6 apart can a sub-tile's
+    // factor vs / vref fall below 2^-6, so only then is the exact form run.
+    // Every wave finds the same answer, so the return is uniform over the
+    // workgroup (and comes before any barrier).
+    float vhi = 0.f, vlo = __builtin_inff();
+    for (int slot = first + lane; slot < end; slot += 64) {
+      const uint32_t pid = static_cast<uint32_t>(pt.row[slot]);
+      const float a = __builtin_fabsf(p.v_scale[static_cast<int64_t>(pid) * Hkv + kvh]);
+      vhi = __builtin_fmaxf(vhi, a);
+      if (a > 0.f) vlo = __builtin_fminf(vlo, a);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      vhi = __builtin_fmaxf(vhi, shfl_xor(vhi, m));
+      vlo = __builtin_fminf(vlo, shfl_xor(vlo, m));
+    }
+    if (__builtin_amdgcn_readfirstlane(vlo < vhi * kFarScale ? 1 : 0)) return false;
+  }
+
+  // ---- LDS (the kernel's): two K/V tile buffers (swizzled rows); for 8-bit
+  // codes also the K and V scales of each buffer's 16-token sub-tiles,
+  // sub_scale[buf][K, V][sub-tile]
+  static_assert(2 * 2 * kBuf == prefill_tile_lds<D>(), "LDS size");
+  char* smem = (char*)smem3;
   auto swz = [](int r, int cidx) __attribute__((always_inline)) {
     return r * kRowBytes + 16 * (cidx ^ ((2 * r) & (kChunks - 1)));
   };
@@ -408,8 +446,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
   };
   // weights 2^x of one half's exponents, 8 per row block (as f16, or as high
   // and low bf16 parts), their row sums, and O += P . V
-  auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x, const float* vfac)
-                     __attribute__((always_inline)) {
+  auto half_pv = [&](auto f16pv, lds_char* vb3, int h, Scores& x, const float* vfac,
+                     bool add_sums = true) __attribute__((always_inline)) {
     constexpr bool kF16 = decltype(f16pv)::value;
     u32x4 phi[RB], plo[RB];
 #pragma unroll
@@ -434,8 +472,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       }
       phi[rb] = u32x4{hi[0], hi[1], hi[2], hi[3]};
       plo[rb] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      if (add_sums) {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) lsum[rb] += pe[w];
+        for (int w = 0; w < 8; ++w) lsum[rb] += pe[w];
+      }
     }
     const int tr_row = 4 * g + (li >> 2);
 #pragma unroll
@@ -458,6 +498,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       }
     }
   };
+  auto scale_o = [&](float f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < kNBlocks; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[rb][nb][e] *= f;
+  };
+
   // One tile: both halves' score MFMAs; the mask (only on tiles that cross a
   // row's last key or the split's end); one lazy-rescale decision per row
   // block for the whole tile (the reference max is raised only when some
@@ -553,8 +602,47 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         vref = vmax;
         inv_vref = 1.f / vmax;
       }
+      bool far[kSub], any_far = false;
 #pragma unroll
-      for (int k = 0; k < kSub; ++k) vfac[k] = vs[k] * inv_vref;
+      for (int k = 0; k < kSub; ++k) {
+        vfac[k] = vs[k] * inv_vref;
+        far[k] = kExact && vfac[k] != 0.f && __builtin_fabsf(vfac[k]) < kFarScale;
+        any_far |= far[k];
+      }
+      if (kExact && any_far) {  // wave-uniform (the scales are)
+        // the near sub-tiles (and every row sum) as usual, the far ones zeroed;
+        // then each far sub-tile alone, its exponents computed again from LDS:
+        // its factor f = m 2^E with |m| in [1, 2) (E at least -60, below which
+        // its share is negligible); O is taken to 2^-E times itself, gets
+        // P . V with weights times m, and comes back -- powers of two, exact
+        // in f32 at these magnitudes
+        float vz[kSub];
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) vz[k] = far[k] ? 0.f : vfac[k];
+        half_pv(f16pv, vb3, 0, x0, vz);
+        half_pv(f16pv, vb3, 1, x1, vz);
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) {
+          if (!far[k]) continue;
+          Scores xr;
+          half_scores(kb, k / 2, xr);
+          half_mask(tile_tok0 + 32 * (k / 2), xr);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xr[rb][q2][e] = __builtin_fmaf(xr[rb][q2][e], c, -msub[rb]);
+          const int ex = max(__builtin_amdgcn_frexp_expf(vfac[k]) - 1, -60);
+          float vk[kSub];
+#pragma unroll
+          for (int k2 = 0; k2 < kSub; ++k2) vk[k2] = k2 == k ? __builtin_ldexpf(vfac[k], -ex) : 0.f;
+          scale_o(__builtin_ldexpf(1.f, -ex));
+          half_pv(f16pv, vb3, k / 2, xr, vk, false);
+          scale_o(__builtin_ldexpf(1.f, ex));
+        }
+        return;
+      }
     }
     half_pv(f16pv, vb3, 0, x0, vfac);
     half_pv(f16pv, vb3, 1, x1, vfac);
@@ -600,7 +688,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       __syncthreads();  // the next tile has landed (the compiler waits for it) and this one is done
     }
   };
-  if constexpr (kQuant) {
+  // 8-bit codes: the tile loop (with the per-sub-tile test for V factors far
+  // below the running reference in the exact form)
+  auto run_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       ref[rb] = kNegInf;
@@ -624,6 +714,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
       if (more) store_tile_q((t + 1) & 1, tok0 + kTile, kr, vr, ks, vs);
       __syncthreads();  // the next tile is in LDS and this one is done
     }
+  };
+  if constexpr (kQuant) {
+    run_q();
   } else {
     run(std::true_type());
   }
@@ -684,6 +777,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_kernel(const Att
         for (int nb = 0; nb < kNBlocks; ++nb) dst[16 * nb + li] = o[rb][nb][e] * inv;
         if (li == 0) p.part_lse[prow] = lse;
       }
+    }
+  }
+  return true;
+}
+
+// The exact form as a separate function: the compiler allocates its registers
+// on their own, so its extra paths cost the common loop nothing.
+// It reads the parameters through a pointer to the kernel's argument segment
+// (a reference to the argument itself would make the kernel copy it to
+// scratch memory and read it from there in the common loop too).
+template <typename T, int D, int PS, int NW, int RB, typename KV>
+__device__ __attribute__((noinline)) void prefill_body_exact(const AttnParams* p,
+                                                             lds_char* smem3,
+                                                             lds_float* sub_scale) {
+  prefill_body<T, D, PS, NW, RB, KV, true>(*p, smem3, sub_scale);
+}
+
+// At D = 64 three workgroups of 4 waves share a compute unit (at most 170
+// VGPRs per lane), at D = 128 two.
+template <typename T, int D, int PS, int NW, int RB, typename KV = KvSame>
+__global__ __launch_bounds__(NW * 64, (D == 64 ? 12 : 8) / NW) void attn_prefill_kernel(
+    const AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[prefill_tile_lds<D>()];
+  __shared__ float sub_scale[KvTraits<KV>::quant ? 2 * 2 * 4 : 1];
+  lds_char* smem3 = (lds_char*)(smem);
+  lds_float* sub3 = (lds_float*)(sub_scale);
+  if (!prefill_body<T, D, PS, NW, RB, KV, false>(p, smem3, sub3)) {
+    if constexpr (KvTraits<KV>::quant) {
+      // the kernel's only argument, at the start of its argument segment
+      const AttnParams* args =
+          (const AttnParams*)(const void*)__builtin_amdgcn_kernarg_segment_ptr();
+      prefill_body_exact<T, D, PS, NW, RB, KV>(args, smem3, sub3);
     }
   }
 }

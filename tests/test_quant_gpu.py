@@ -5,6 +5,8 @@ Unreferenced pages carry NaN scales and NaN (fp8) or -128 (int8) codes, and
 last-page tails poison codes, so a stray read shows up in the comparison.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -168,3 +170,77 @@ def test_full_size_full_batch(name):
     out, lse, _ = run(w, 0)
     worst = compare_every_sequence(w, out, lse, chunk=16)
     say(f"{name}: all 256 sequences within tolerance, max |out err| {worst:.2e}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_v_scales_span_2m16_to_1(kind, d):
+    """The recipe's V scales times factors log-uniform over 2^-16 .. 1 per page
+    and kv head, with random signs (K scales times 2^-6 .. 1), in the
+    shared-tile prefill kernel: most tiles meet V scales more than 2^6 below
+    the largest one so far.  (Factors <= 1 keep the values within the
+    recipe's magnitude, for which the absolute part of the bar is sized.)"""
+    say(f"prefill, V scales over 2^-16..1, {kind}, D={d}")
+    w = make_custom("f16" if d == 64 else "bf16", [400, 130, 900], 16, 4, d, 16, seq_q=32,
+                    causal=True, seed=47, device=DEV, kv=kind)
+    shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
+    assert pa.describe_plan(shape, 0)["kernel"] == "shared_tile"
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(48)
+    for name, span in (("k_scale", 6.0), ("v_scale", 16.0)):
+        sc = getattr(w, name)
+        mag = torch.exp2(-span * torch.rand(sc.shape, generator=gen, device=DEV))
+        sign = torch.where(torch.rand(sc.shape, generator=gen, device=DEV) < 0.3, -1.0, 1.0)
+        setattr(w, name, sc * sign * mag)
+    for splits in (1, 3):
+        out, lse, ws = run(w, splits, True)
+        check(w, out, lse, ws, splits, True)
+
+
+CODE_ONE = {"int8": 1, "fp8_e4m3": 0x38}      # the code of 1.0
+CODE_BIG = {"int8": 127, "fp8_e4m3": 0x7E}    # 127 and 448
+
+
+def far_apart_v_scales(kind, d, seed):
+    """Every row's first page: V scale 2^14 and V codes 0, K codes that give
+    its 16 keys the row's largest score (0.3567); every other page: V scale
+    2^-6 (2^-20 of the first) with the largest V codes and score 0.  The
+    other keys then weigh e^-0.3567 = 0.7 of the first ones each and carry
+    the whole output, about 1.9 (int8) or 6.7 (fp8): V weights formed relative
+    to the first page's scale alone would sit 2^-20 below it, among f16's
+    subnormals, about 2% off -- beyond the bound."""
+    lens = [512, 300]
+    w = make_custom("f16" if d == 64 else "bf16", lens, 16, 4, d, 16, seq_q=32, causal=True,
+                    seed=seed, device=DEV, kv=kind)
+    w.q.zero_()
+    w.q[..., 0] = 1.0
+    kc, vc = w.k_cache.view(torch.uint8), w.v_cache.view(torch.uint8)
+    for b, length in enumerate(lens):
+        t = torch.arange(length)
+        pages = w.table_host[b, t // 16].long().to(DEV)
+        slots = (t % 16).to(DEV)
+        first = pages[:16]
+        kc[pages, slots] = 0
+        vc[pages, slots] = CODE_BIG[kind]
+        kc[first, slots[:16], :, 0] = CODE_ONE[kind]
+        vc[first, slots[:16]] = 0
+        w.k_scale[pages] = 1.0
+        w.v_scale[pages] = 2.0 ** -6
+        w.k_scale[first[0]] = 0.3567 * math.sqrt(d)
+        w.v_scale[first[0]] = 2.0 ** 14
+    torch.cuda.synchronize()
+    return w
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_v_scales_far_below_the_largest(kind, d):
+    say(f"prefill, V scales 2^-20 below the largest met, {kind}, D={d}")
+    w = far_apart_v_scales(kind, d, 49)
+    shape = pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table)
+    assert pa.describe_plan(shape, 0)["kernel"] == "shared_tile"
+    xo, _ = oracle(w, True)
+    assert np.abs(xo).max() > 1.5 and np.abs(xo).min() > 1.5
+    for splits in (1, 3):
+        out, lse, ws = run(w, splits, True)
+        check(w, out, lse, ws, splits, True)
