@@ -472,10 +472,8 @@ __device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem
       }
       phi[rb] = u32x4{hi[0], hi[1], hi[2], hi[3]};
       plo[rb] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      if (add_sums) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) lsum[rb] += pe[w];
-      }
+      if (add_sums)  // as a tree: a serial chain of dependent additions stalls the wave
+        lsum[rb] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     }
     const int tr_row = 4 * g + (li >> 2);
 #pragma unroll

@@ -399,9 +399,12 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         y = __builtin_fmaf(y, c, -msub[rb]);
         pe[k] = fast_exp2(y);
       }
-      float tsum = 0.f;
+      // the 16 weights summed as a tree: a serial chain of 16 dependent
+      // additions left the wave stalled on each one
+      float s8[8];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) tsum += pe[k];
+      for (int k = 0; k < 8; ++k) s8[k] = pe[2 * k] + pe[2 * k + 1];
+      float tsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
       const bool check = ref[rb] == kNegInf || !(tsum <= 256.f);  // 2^kSlack
       if (__builtin_amdgcn_ballot_w64(check) != 0) {  // wave-uniform, rare
         float tmax = kNegInf;
@@ -475,8 +478,28 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     if (t > 0 && active(t - 1)) {
       pv_half(std::false_type(), (kB + kNBuf - 1) % kNBuf, 0, pw[0], no_lo);
       pv_half(std::false_type(), (kB + kNBuf - 1) % kNBuf, 1, pw[1], no_lo);
+      // LDS reads 8 ahead of the MFMAs that use them (32 transposing reads,
+      // 32 MFMAs): left to itself the scheduler kept two reads in flight and
+      // each pair of MFMAs waited for its operands
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
-    if (t < n_tiles && active(t)) qk(kB, x);
+    if (t < n_tiles && active(t)) {
+      qk(kB, x);
+      // 16 K-operand reads, 32 MFMAs (two per read), reads 4 ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
   };
   // V(t): this team's loads of a later tile (team 0 rows 0-31 of tile t+1,
   // team 1 rows 32-63 of tile t+2), then the softmax of tile t
