@@ -190,6 +190,109 @@ __device__ __forceinline__ void widen16(const u32x4& w, u32x4& lo, u32x4& hi) {
   hi = u32x4{packed[4], packed[5], packed[6], packed[7]};
 }
 
+// The end of the matrix-core decode kernels: merges the partial softmax states
+// of the waves that share a kv head, then writes the rows (out and lse, or the
+// split partials).  Wave w left at smem + w * kPerWave: o [kRows][D] (f32,
+// unnormalised), then ref [kRows] (running maximum, base 2) and l [kRows] (row
+// sum).  Waves hg * WPH .. hg * WPH + WPH - 1 serve the workgroup's kv head hg.
+// Call after a workgroup barrier that follows those writes.
+//
+// Two passes.  First one thread per (kv head, row) forms each wave's weight
+// 2^(ref_w - max) and the row's total sum, writes the row's lse, and leaves the
+// weights in the l slots and the total in the first wave's ref slot.  Then
+// one thread per output element sums the weighted o values of the waves.  The
+// weights are formed once per row, not once per element, and the wave count
+// is a compile-time constant, so each pass issues all its LDS reads of an
+// element at once (one round trip); with a run-time wave count every wave's
+// reads were a separate round trip.
+template <typename T, int D, int kRows, int NW, int kPerWave, int WPH>
+__device__ __forceinline__ void merge_wave_states_n(const AttnParams& p, char* smem, int kpw,
+                                                    int rg, int b, int split) {
+  const int S = p.num_splits;
+  const int G = p.group;
+  const int Sq = p.seq_q;
+  const int Hq = p.num_q_heads;
+  auto wave_f = [&](int w) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(smem + w * kPerWave);
+  };
+  auto row_id = [&](int hg, int r_lin) __attribute__((always_inline)) {
+    const int i = r_lin / G;
+    return (b * Sq + i) * Hq + (blockIdx.y * kpw + hg) * G + (r_lin - i * G);
+  };
+  for (int t = threadIdx.x; t < kpw * kRows; t += NW * 64) {
+    const int hg = t / kRows;
+    const int r = t - hg * kRows;
+    const int r_lin = rg * kRows + r;
+    if (r_lin >= p.rows_per_kvh) continue;
+    float wr[WPH], wl[WPH];
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) {
+      wr[k] = wave_f(hg * WPH + k)[kRows * D + r];
+      wl[k] = wave_f(hg * WPH + k)[kRows * D + kRows + r];
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) mx = __builtin_fmaxf(mx, wr[k]);
+    const float wsub = mx == kNegInf ? 0.f : mx;
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) {
+      // a wave with no valid key for this row has ref = -inf and l = 0, o = 0
+      const float f = wr[k] == kNegInf ? 0.f : fast_exp2(wr[k] - wsub);
+      tot += f * wl[k];
+      wave_f(hg * WPH + k)[kRows * D + kRows + r] = f;
+    }
+    wave_f(hg * WPH)[kRows * D + r] = tot;
+    const float lse = tot > 0.f ? (mx + log2f(tot)) * kLn2 : kNegInf;
+    const int rid = row_id(hg, r_lin);
+    if (S == 1) {
+      if (p.lse != nullptr) p.lse[rid] = lse;
+    } else {
+      p.part_lse[static_cast<int64_t>(rid) * S + split] = lse;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kpw * kRows * D; idx += NW * 64) {
+    const int hg = idx / (kRows * D);
+    const int r = (idx / D) % kRows;
+    const int d = idx % D;
+    const int r_lin = rg * kRows + r;
+    if (r_lin >= p.rows_per_kvh) continue;
+    const float tot = wave_f(hg * WPH)[kRows * D + r];
+    float f[WPH], o[WPH];
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) {
+      f[k] = wave_f(hg * WPH + k)[kRows * D + kRows + r];
+      o[k] = wave_f(hg * WPH + k)[r * D + d];
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) a += f[k] * o[k];
+    const float out = tot > 0.f ? a / tot : 0.f;
+    const int rid = row_id(hg, r_lin);
+    if (S == 1)
+      static_cast<T*>(p.out)[static_cast<int64_t>(rid) * D + d] = from_float<T>(out);
+    else
+      p.part_out[(static_cast<int64_t>(rid) * S + split) * D + d] = out;
+  }
+}
+
+// kpw kv heads per workgroup, NW / kpw waves per head (1, 2, 4 or 8).
+template <typename T, int D, int kRows, int NW, int kPerWave>
+__device__ __forceinline__ void merge_wave_states(const AttnParams& p, char* smem, int kpw, int rg,
+                                                  int b, int split) {
+  const int wph = NW / kpw;
+  if (wph == 1) {
+    merge_wave_states_n<T, D, kRows, NW, kPerWave, 1>(p, smem, kpw, rg, b, split);
+  } else if (wph == 2) {
+    merge_wave_states_n<T, D, kRows, NW, kPerWave, 2>(p, smem, kpw, rg, b, split);
+  } else if (wph == 4 || NW == 4) {
+    merge_wave_states_n<T, D, kRows, NW, kPerWave, (NW < 4 ? NW : 4)>(p, smem, kpw, rg, b, split);
+  } else {
+    merge_wave_states_n<T, D, kRows, NW, kPerWave, NW>(p, smem, kpw, rg, b, split);
+  }
+}
+
 // T: bf16_t or f16_t (q, out and the MFMA operands); KV: KvSame (caches of
 // T) or KvI8 / KvFp8 (8-bit codes with p.k_scale / p.v_scale); D: head dim
 // (= Dv, a multiple of 32; >= 64 for codes); PS: tokens per page (a multiple
@@ -549,44 +652,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(const AttnParams p) 
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < kpw * 16 * D; idx += NW * 64) {
-    const int hg = idx / (16 * D);
-    const int r = (idx / D) % 16;
-    const int d = idx % D;
-    const int r_lin = rg * 16 + r;
-    if (r_lin >= p.rows_per_kvh) continue;
-    const int i = r_lin / G;
-    const int rid = (b * Sq + i) * Hq + (blockIdx.y * kpw + hg) * G + (r_lin - i * G);
-    float mx = kNegInf;
-    for (int w = hg * wph; w < (hg + 1) * wph; ++w)
-      mx = __builtin_fmaxf(mx, reinterpret_cast<const float*>(smem + w * kPerWave)[16 * D + r]);
-    const float wsub = mx == kNegInf ? 0.f : mx;
-    float tot = 0.f, a = 0.f;
-    for (int w = hg * wph; w < (hg + 1) * wph; ++w) {
-      const float* wo = reinterpret_cast<const float*>(smem + w * kPerWave);
-      const float wr = wo[16 * D + r];
-      // a wave with no valid key for this row has ref = -inf and l = 0, o = 0
-      const float f = wr == kNegInf ? 0.f : fast_exp2(wr - wsub);
-      tot += f * wo[16 * D + 16 + r];
-      a += f * wo[r * D + d];
-    }
-    float out, lse;
-    if (tot > 0.f) {
-      out = a / tot;
-      lse = (mx + log2f(tot)) * kLn2;
-    } else {
-      out = 0.f;
-      lse = kNegInf;
-    }
-    if (S == 1) {
-      static_cast<T*>(p.out)[static_cast<int64_t>(rid) * D + d] = from_float<T>(out);
-      if (d == 0 && p.lse != nullptr) p.lse[rid] = lse;
-    } else {
-      const int64_t prow = static_cast<int64_t>(rid) * S + split;
-      p.part_out[prow * D + d] = out;
-      if (d == 0) p.part_lse[prow] = lse;
-    }
-  }
+  merge_wave_states<T, D, 16, NW, kPerWave>(p, smem, kpw, rg, b, split);
 }
 
 }  // namespace pa

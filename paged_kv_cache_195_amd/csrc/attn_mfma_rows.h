@@ -413,44 +413,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_rows_kernel(const AttnParam
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < kpw * kRows * D; idx += NW * 64) {
-    const int hg = idx / (kRows * D);
-    const int r = (idx / D) % kRows;
-    const int d = idx % D;
-    const int r_lin = rg * kRows + r;
-    if (r_lin >= p.rows_per_kvh) continue;
-    const int i = r_lin / G;
-    const int rid = (b * Sq + i) * Hq + (blockIdx.y * kpw + hg) * G + (r_lin - i * G);
-    float mx = kNegInf;
-    for (int w = hg * wph; w < (hg + 1) * wph; ++w)
-      mx = __builtin_fmaxf(mx, reinterpret_cast<const float*>(smem + w * kPerWave)[kRows * D + r]);
-    const float wsub = mx == kNegInf ? 0.f : mx;
-    float tot = 0.f, a = 0.f;
-    for (int w = hg * wph; w < (hg + 1) * wph; ++w) {
-      const float* wo = reinterpret_cast<const float*>(smem + w * kPerWave);
-      const float wr = wo[kRows * D + r];
-      // a wave with no valid key for this row has ref = -inf and l = 0, o = 0
-      const float f = wr == kNegInf ? 0.f : fast_exp2(wr - wsub);
-      tot += f * wo[kRows * D + kRows + r];
-      a += f * wo[r * D + d];
-    }
-    float out, lse;
-    if (tot > 0.f) {
-      out = a / tot;
-      lse = (mx + log2f(tot)) * kLn2;
-    } else {
-      out = 0.f;
-      lse = kNegInf;
-    }
-    if (S == 1) {
-      static_cast<T*>(p.out)[static_cast<int64_t>(rid) * D + d] = from_float<T>(out);
-      if (d == 0 && p.lse != nullptr) p.lse[rid] = lse;
-    } else {
-      const int64_t prow = static_cast<int64_t>(rid) * S + split;
-      p.part_out[prow * D + d] = out;
-      if (d == 0) p.part_lse[prow] = lse;
-    }
-  }
+  merge_wave_states<T, D, kRows, NW, kPerWave>(p, smem, kpw, rg, b, split);
 }
 
 }  // namespace pa
