@@ -47,6 +47,7 @@ TRAFFIC_FILES = {
     "qwen3_235b_decode": os.path.join(ROOT, "profiles", "attn_decode_qwen3_235b_traffic.md"),
     "llama3_8b_decode_int8": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_int8_traffic.md"),
     "llama3_8b_decode_fp8": os.path.join(ROOT, "profiles", "attn_decode_llama3_8b_fp8_traffic.md"),
+    "decode_g32_b256": os.path.join(ROOT, "profiles", "attn_decode_g32_b256_traffic.md"),
 }
 KERNEL_SOURCES = os.path.join(ROOT, "paged_kv_cache_195_amd", "csrc")
 # the sources each workload's kernel is built from (host planning included)
@@ -57,6 +58,7 @@ TRAFFIC_SOURCES = {
     "qwen3_235b_decode": _COMMON + _MFMA + ["attn_mfma_bf16.hip"],
     "llama3_8b_decode_int8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],
     "llama3_8b_decode_fp8": _COMMON + _MFMA + ["attn_mfma_q_bf16.hip"],
+    "decode_g32_b256": _COMMON + _MFMA + ["attn_mfma_rows.h", "attn_mfma_bf16.hip"],
 }
 
 

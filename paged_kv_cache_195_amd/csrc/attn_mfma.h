@@ -252,28 +252,50 @@ __device__ __forceinline__ void merge_wave_states_n(const AttnParams& p, char* s
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kpw * kRows * D; idx += NW * 64) {
-    const int hg = idx / (kRows * D);
-    const int r = (idx / D) % kRows;
-    const int d = idx % D;
+  // four consecutive elements of a row per thread: one 16-byte LDS read per
+  // wave, and one 8-byte store when the output allows it
+  const bool out8 = (reinterpret_cast<uintptr_t>(p.out) & 7u) == 0;
+  for (int idx = threadIdx.x; idx < kpw * kRows * (D / 4); idx += NW * 64) {
+    const int e0 = 4 * idx;
+    const int hg = e0 / (kRows * D);
+    const int r = (e0 / D) % kRows;
+    const int d0 = e0 % D;
     const int r_lin = rg * kRows + r;
     if (r_lin >= p.rows_per_kvh) continue;
     const float tot = wave_f(hg * WPH)[kRows * D + r];
-    float f[WPH], o[WPH];
+    float f[WPH];
+    f32x4 o[WPH];
 #pragma unroll
     for (int k = 0; k < WPH; ++k) {
       f[k] = wave_f(hg * WPH + k)[kRows * D + kRows + r];
-      o[k] = wave_f(hg * WPH + k)[r * D + d];
+      o[k] = *reinterpret_cast<const f32x4*>(wave_f(hg * WPH + k) + r * D + d0);
     }
-    float a = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < WPH; ++k) a += f[k] * o[k];
-    const float out = tot > 0.f ? a / tot : 0.f;
+    for (int k = 0; k < WPH; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] += f[k] * o[k][c];
+    f32x4 out;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = tot > 0.f ? a[c] / tot : 0.f;
     const int rid = row_id(hg, r_lin);
-    if (S == 1)
-      static_cast<T*>(p.out)[static_cast<int64_t>(rid) * D + d] = from_float<T>(out);
-    else
-      p.part_out[(static_cast<int64_t>(rid) * S + split) * D + d] = out;
+    if (S == 1) {
+      T* dst = static_cast<T*>(p.out) + static_cast<int64_t>(rid) * D + d0;
+      if (out8) {
+        uint32_t w[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          w[c] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_float<T>(out[2 * c]))) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_float<T>(out[2 * c + 1])))
+                  << 16);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = from_float<T>(out[c]);
+      }
+    } else {
+      *reinterpret_cast<f32x4*>(p.part_out + (static_cast<int64_t>(rid) * S + split) * D + d0) = out;
+    }
   }
 }
 
