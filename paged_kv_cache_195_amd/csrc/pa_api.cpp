@@ -59,8 +59,10 @@ int check_shape(const pa_shape* s, bool decode) {
       static_cast<int64_t>(s->page_size) * s->num_kv_heads * s->head_dim_qk * elem;
   if (page_bytes > INT32_MAX) return PA_EINVAL;
   if (s->num_pages > INT64_MAX / page_bytes) return PA_EINVAL;
-  if (static_cast<int64_t>(s->batch - 1) * s->block_table_stride >
-      INT64_MAX - s->max_pages_per_seq)
+  // The last row's end, (B - 1) * stride + W, must be representable; tested
+  // by division so the check itself cannot overflow.
+  if (s->batch > 1 &&
+      s->block_table_stride > (INT64_MAX - s->max_pages_per_seq) / (s->batch - 1))
     return PA_EINVAL;
   // Envelope of the compiled kernels (grid y = Hkv and z = B are 16-bit).
   if (s->batch > 65535 || s->num_kv_heads > 65535) return PA_EUNSUPPORTED;
