@@ -26,7 +26,11 @@ hipError_t launch_attn_valu_dp(const AttnParams& p, const AttnPlan& plan, int ba
     case 1: return launch_attn_valu_cfg<T, D, PS, 1>(p, plan, batch, stream);
     case 2: return launch_attn_valu_cfg<T, D, PS, 2>(p, plan, batch, stream);
     case 4: return launch_attn_valu_cfg<T, D, PS, 4>(p, plan, batch, stream);
-    case 8: return launch_attn_valu_cfg<T, D, PS, 8>(p, plan, batch, stream);
+    case 8:
+      if constexpr (valu_max_rows(sizeof(T), D, PS) >= 8)
+        return launch_attn_valu_cfg<T, D, PS, 8>(p, plan, batch, stream);
+      else
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

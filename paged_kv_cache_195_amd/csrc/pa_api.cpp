@@ -116,6 +116,8 @@ pa::AttnPlan plan_for(const pa_shape* s, int num_splits) {
                      : pa::kMfmaWaves;
   } else {
     plan.rows_per_wg = rows_per_wg(rows_per_kvh);
+    const int max_rows = pa::valu_max_rows(elem, s->head_dim_qk, s->page_size);
+    if (plan.rows_per_wg > max_rows) plan.rows_per_wg = max_rows;
     plan.waves = pa::valu_config(elem, s->head_dim_qk, s->page_size, plan.rows_per_wg).waves;
   }
   plan.row_groups = static_cast<int>((rows_per_kvh + plan.rows_per_wg - 1) / plan.rows_per_wg);

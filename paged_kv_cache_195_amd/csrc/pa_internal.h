@@ -64,6 +64,13 @@ constexpr ValuConfig valu_config(int elem_bytes, int head_dim, int page_size, in
   return (page_size * head_dim * elem_bytes / 1024 <= 4 && rows_per_wg <= 4) ? ValuConfig{16, 0}
                                                                               : ValuConfig{8, 0};
 }
+// Most rows per workgroup of the vector-ALU kernel: 8, but 4 for f32 at D = 128
+// with 32-token pages, whose 8-row form needs more than 256 VGPRs (a page of K
+// and V is 128 registers per lane there) and spilled 193 of them; two 4-row
+// groups read the pages twice instead.
+constexpr int valu_max_rows(int elem_bytes, int head_dim, int page_size) {
+  return (elem_bytes == 4 && head_dim == 128 && page_size == 32) ? 4 : 8;
+}
 
 // The matrix-core kernel: 16 rows per kv head and workgroup, 8 waves.  It
 // serves every 16-bit and 8-bit cache (the shared-tile prefill kernel aside):
