@@ -587,37 +587,74 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     }
   }
 
-  // ---- finish: normalize and write; row 4 g + e of the O layout takes its
-  // sum and its reference from lane 4 g + e
+  // ---- finish: normalize and write.  After the two exchanges every lane
+  // holds row li's sum and reference, so it forms that row's 1/l and LSE
+  // once; row 4 g + e of the O layout takes its 1/l from lane 4 g + e.  Two
+  // rows' values are rounded to the output type in one packed conversion.
+  typedef __attribute__((ext_vector_type(2))) float f32x2v;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v;
+  auto pack2 = [](float a, float b) __attribute__((always_inline)) {
+    const f32x2v v = {a, b};
+    if constexpr (std::is_same<T, bf16_t>::value)
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
+  };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     lsum[rb] += shfl_xor(lsum[rb], 16);
     lsum[rb] += shfl_xor(lsum[rb], 32);
+    const bool any = lsum[rb] > 0.f;  // no valid key: (0, -inf) instead of 0/0
+    const float inv_row = any ? 1.f / lsum[rb] : 0.f;
+    const float lse_row = any ? (ref[rb] + log2f(lsum[rb])) * kLn2 : kNegInf;
+    auto row_id = [&](int r_lin) __attribute__((always_inline)) {
+      const int i = r_lin / G;
+      return (b * Sq + i) * Hq + kvh * G + (r_lin - i * G);
+    };
+    {
+      const int r_lin = wave_first + 16 * rb + li;
+      if (g == 0 && r_lin < p.rows_per_kvh) {
+        const int rid = row_id(r_lin);
+        if (S == 1) {
+          if (p.lse != nullptr) p.lse[rid] = lse_row;
+        } else {
+          p.part_lse[static_cast<int64_t>(rid) * S + split] = lse_row;
+        }
+      }
+    }
+    float inv[4];
+    int rid[4];
+    bool valid[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int src = (4 * g + e) << 2;
-      const float le = __builtin_bit_cast(
-          float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, lsum[rb])));
-      const float re = __builtin_bit_cast(
-          float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, ref[rb])));
+      inv[e] = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute((4 * g + e) << 2, __builtin_bit_cast(int, inv_row)));
       const int r_lin = wave_first + 16 * rb + 4 * g + e;
-      if (r_lin >= p.rows_per_kvh) continue;
-      const int i = r_lin / G;
-      const int rid = (b * Sq + i) * Hq + kvh * G + (r_lin - i * G);
-      const bool any = le > 0.f;  // no valid key: (0, -inf) instead of 0/0
-      const float lse = any ? (re + log2f(le)) * kLn2 : kNegInf;
-      const float inv = any ? 1.f / le : 0.f;
-      if (S == 1) {
-        T* dst = static_cast<T*>(p.out) + static_cast<int64_t>(rid) * D;
+      valid[e] = r_lin < p.rows_per_kvh;
+      rid[e] = valid[e] ? row_id(r_lin) : 0;
+    }
+    if (S == 1) {
 #pragma unroll
-        for (int nb = 0; nb < kNBlocks; ++nb) dst[16 * nb + li] = from_float<T>(o[rb][nb][e] * inv);
-        if (li == 0 && p.lse != nullptr) p.lse[rid] = lse;
-      } else {
-        const int64_t prow = static_cast<int64_t>(rid) * S + split;
-        float* dst = p.part_out + prow * D;
+      for (int ep = 0; ep < 2; ++ep) {
+        uint16_t* d0 = reinterpret_cast<uint16_t*>(static_cast<T*>(p.out) +
+                                                   static_cast<int64_t>(rid[2 * ep]) * D);
+        uint16_t* d1 = reinterpret_cast<uint16_t*>(static_cast<T*>(p.out) +
+                                                   static_cast<int64_t>(rid[2 * ep + 1]) * D);
 #pragma unroll
-        for (int nb = 0; nb < kNBlocks; ++nb) dst[16 * nb + li] = o[rb][nb][e] * inv;
-        if (li == 0) p.part_lse[prow] = lse;
+        for (int nb = 0; nb < kNBlocks; ++nb) {
+          const uint32_t pk = pack2(o[rb][nb][2 * ep] * inv[2 * ep],
+                                    o[rb][nb][2 * ep + 1] * inv[2 * ep + 1]);
+          if (valid[2 * ep]) d0[16 * nb + li] = static_cast<uint16_t>(pk);
+          if (valid[2 * ep + 1]) d1[16 * nb + li] = static_cast<uint16_t>(pk >> 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!valid[e]) continue;
+        float* dst = p.part_out + (static_cast<int64_t>(rid[e]) * S + split) * D;
+#pragma unroll
+        for (int nb = 0; nb < kNBlocks; ++nb) dst[16 * nb + li] = o[rb][nb][e] * inv[e];
       }
     }
   }

@@ -109,15 +109,12 @@ __device__ __forceinline__ float from_float<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ f16_t from_float<f16_t>(float x) { return static_cast<f16_t>(x); }
 
+// bf16: gfx950's conversion instruction (v_cvt_pk_bf16_f32) rounds to nearest
+// even and quiets NaN in one instruction, where the integer form took six.
 template <>
 __device__ __forceinline__ bf16_t from_float<bf16_t>(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
   bf16_t r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) {
-    r.bits = static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
-  } else {
-    r.bits = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-  }
+  r.bits = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
   return r;
 }
 
