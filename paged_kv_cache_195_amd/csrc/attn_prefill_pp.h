@@ -390,23 +390,35 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                   tile_tok0 + 32 * h + 16 * q2 + 4 * g + e < lim ? xs[h][rb][q2][e] : kNegInf;
       }
     }
+    // both row blocks' exponentials first (one stream of independent
+    // instructions), then one wave-wide test for the rare cases
+    float pe[RB][16];
+    float tsum[RB];
+    bool check = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float pe[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         float& y = xs[k >> 3][rb][(k >> 2) & 1][k & 3];
         y = __builtin_fmaf(y, c, -msub[rb]);
-        pe[k] = fast_exp2(y);
+        pe[rb][k] = fast_exp2(y);
       }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       // the 16 weights summed as a tree: a serial chain of 16 dependent
       // additions left the wave stalled on each one
       float s8[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s8[k] = pe[2 * k] + pe[2 * k + 1];
-      float tsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-      const bool check = ref[rb] == kNegInf || !(tsum <= 256.f);  // 2^kSlack
-      if (__builtin_amdgcn_ballot_w64(check) != 0) {  // wave-uniform, rare
+      for (int k = 0; k < 8; ++k) s8[k] = pe[rb][2 * k] + pe[rb][2 * k + 1];
+      tsum[rb] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+      check = check || ref[rb] == kNegInf || !(tsum[rb] <= 256.f);  // 2^kSlack
+    }
+    if (__builtin_amdgcn_ballot_w64(check) != 0) {  // wave-uniform, rare
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bool check_rb = ref[rb] == kNegInf || !(tsum[rb] <= 256.f);
+        if (__builtin_amdgcn_ballot_w64(check_rb) == 0) continue;
         float tmax = kNegInf;
 #pragma unroll
         for (int k = 0; k < 16; ++k) tmax = __builtin_fmaxf(tmax, xs[k >> 3][rb][(k >> 2) & 1][k & 3]);
@@ -421,13 +433,13 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
           ref[rb] = nref;
           msub[rb] = nsub;
           lsum[rb] *= alpha;
-          tsum = 0.f;
+          tsum[rb] = 0.f;
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             float& y = xs[k >> 3][rb][(k >> 2) & 1][k & 3];
             y += shift;
-            pe[k] = fast_exp2(y);
-            tsum += pe[k];
+            pe[rb][k] = fast_exp2(y);
+            tsum[rb] += pe[rb][k];
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -439,12 +451,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
           }
         }
       }
-      lsum[rb] += tsum;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      lsum[rb] += tsum[rb];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-          pw[h][rb][w] = f32x2_to_f16x2(pe[8 * h + 2 * w], pe[8 * h + 2 * w + 1]);
+          pw[h][rb][w] = f32x2_to_f16x2(pe[rb][8 * h + 2 * w], pe[rb][8 * h + 2 * w + 1]);
     }
   };
   const std::true_type f16v;
