@@ -253,6 +253,23 @@ def test_envelope_decode(dtype, d, ps, hq, hkv, splits):
     assert_close(lse, xl, torch.float32, "lse")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_f32_d128_page32_eight_rows_take_two_row_groups(splits):
+    """f32 caches at D = 128 with 32-token pages run at most 4 rows per
+    workgroup on the vector-ALU kernel (its 8-row form needs more than 256
+    VGPRs): 8 rows per kv head take two row groups that read the pages twice."""
+    say(f"f32 D=128 page 32 G=8 S={splits}")
+    w = make_custom("f32", [3, 70, 129], 16, 2, 128, 32, seed=8, device=DEV)
+    plan = pa.describe_plan(pa.make_shape(w.q, w.k_cache, w.v_cache, w.block_table), splits)
+    assert (plan["kernel"], plan["rows_per_workgroup"], plan["row_groups"]) == ("valu", 4, 2)
+    out, lse, ws = run(w, splits, return_workspace=True)
+    xo, xl = oracle_full(w)
+    assert_close(out, xo, torch.float32, "out")
+    assert_close(lse, xl, torch.float32, "lse")
+    if splits > 1:
+        check_partials(w, splits, ws)
+
+
 @pytest.mark.parametrize("seq_q,lens", [(5, [3, 5, 40]), (16, [16, 100, 0]), (24, [7, 64, 200])])
 @pytest.mark.parametrize("splits", [1, 3])
 def test_causal_prefill_gqa(seq_q, lens, splits):
