@@ -20,9 +20,11 @@
 // teams one phase apart (K in M(t), V in M(t+1)), so a buffer is busy for
 // four phases.  Team 0 loads rows 0-31 of tile t+1 during its V(t), team 1
 // rows 32-63 of tile t+2 during its V(t); each wave 8 rows, K straight into
-// LDS (global_load_lds_dwordx4), V through registers.  The V phase reads no
-// LDS, so those loads overlap the softmax and the barrier that ends the
-// phase is the first wait for them.
+// LDS (global_load_lds_dwordx4); V of f16 caches straight into LDS as well
+// (a buffer load whose range ends at the split's last token, so rows past it
+// arrive as zeros), V of bf16 caches through registers to be converted.  The
+// V phase reads no LDS, so those loads overlap the softmax and the barrier
+// that ends the phase is the first wait for them.
 //
 // The arithmetic per tile is that of the single-team prefill kernel: S^T =
 // K . Q^T with v_mfma_f32_16x16x32 (K from LDS, Q^T in registers), the mask
@@ -66,6 +68,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   constexpr int kNBuf = 3;
   constexpr float kSlack = 8.f;
   constexpr bool kConvertV = std::is_same<T, bf16_t>::value;
+  // V already f16 in memory: straight into LDS like K, no registers
+  constexpr bool kVDma = !kConvertV;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,7 +197,24 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         const int lds_off = buf * 2 * kBuf + (row0 + jl * kRowsPerLoad) * kRowBytes;
         __builtin_amdgcn_global_load_lds((global_ptr)(kbase + base + off),
                                          (lds_ptr)(smem3 + lds_off), 16, 0, 0);
-        vr[jl] = *reinterpret_cast<const u32x4*>(vbase + base + off);
+        if constexpr (!kVDma) vr[jl] = *reinterpret_cast<const u32x4*>(vbase + base + off);
+      }
+      if constexpr (kVDma) {
+        // a buffer resource whose range ends at tok_end: rows past it land
+        // in LDS as zeros (the sequence's last page may hold anything there)
+        const int rows = min(kRowsPerWave, tok_end - tok);
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(vbase) + base + static_cast<int64_t>(in_page) * Hkv * kRowBytes, 0,
+            rows * Hkv * kRowBytes, 0x00020000);
+#pragma unroll
+        for (int jl = 0; jl < kLoads; ++jl) {
+          const int r = row0 + jl * kRowsPerLoad + lr;
+          const int chunk = lc ^ ((2 * r) & (kChunks - 1));
+          const int voff = ((jl * kRowsPerLoad + lr) * Hkv + kvh) * kRowBytes + 16 * chunk;
+          const int lds_off = buf * 2 * kBuf + kBuf + (row0 + jl * kRowsPerLoad) * kRowBytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(smem3 + lds_off), 16, voff, 0,
+                                                   0, 0);
+        }
       }
     }
   };
@@ -216,7 +237,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         return w;
       }
     };
-    if (__builtin_expect(tile_tok0 + row0 + kRowsPerWave <= tok_end, 1)) {  // wave-uniform
+    if constexpr (kVDma && decltype(f16v)::value) {
+      // loaded straight into LDS; a wave that loaded nothing writes zeros
+      if (tile_tok0 + row0 >= tok_end) {
+#pragma unroll
+        for (int jl = 0; jl < kLoads; ++jl)
+          *reinterpret_cast<u32x4*>(vb + (row0 + jl * kRowsPerLoad) * kRowBytes + 16 * lane) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
+    } else if (__builtin_expect(tile_tok0 + row0 + kRowsPerWave <= tok_end, 1)) {  // wave-uniform
 #pragma unroll
       for (int jl = 0; jl < kLoads; ++jl)
         *reinterpret_cast<u32x4*>(vb + (row0 + jl * kRowsPerLoad) * kRowBytes + 16 * lane) =

@@ -446,21 +446,25 @@ def test_prefill_kernel_cases(dtype, d, ps, hq, hkv, seq_q, lens, causal, splits
         check_partials(w, splits, ws, causal=causal)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("seq_q", [64, 70])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_prefill_two_team_tile_counts(causal, seq_q, splits):
+def test_prefill_two_team_tile_counts(dtype, causal, seq_q, splits):
     """At D=128 the prefill kernel runs two teams of waves one phase apart
     over a ring of three 64-token tile buffers, its loop unrolled by three.
     Lengths give every tile count from 0 to 8 (each residue mod 3, ragged
-    last tiles); Sq=70 adds a second row group whose only rows lie in one
-    partly filled wave, so seven of its eight waves only load and wait."""
+    last tiles, NaN in the last pages past each length); Sq=70 adds a second
+    row group whose only rows lie in one partly filled wave, so seven of its
+    eight waves only load and wait.  f16 V goes straight into LDS through a
+    buffer load whose range ends at the split's last token (the rows past it
+    must arrive as zeros), bf16 V through registers."""
     lens = [0, 1, 64, 65, 128, 129, 192, 255, 300, 449, 512]
-    say(f"prefill two-team bf16 D=128 Sq={seq_q} lens={lens} causal={causal} S={splits}")
-    w = make_custom("bf16", lens, 8, 2, 128, 16, seq_q=seq_q, causal=causal, seed=26, device=DEV)
+    say(f"prefill two-team {dtype} D=128 Sq={seq_q} lens={lens} causal={causal} S={splits}")
+    w = make_custom(dtype, lens, 8, 2, 128, 16, seq_q=seq_q, causal=causal, seed=26, device=DEV)
     out, lse, ws = run(w, splits, return_workspace=True, causal=causal)
     xo, xl = oracle_full(w, causal=causal)
-    assert_close(out, xo, torch.bfloat16, "out")
+    assert_close(out, xo, {"f16": torch.float16, "bf16": torch.bfloat16}[dtype], "out")
     assert_close(lse, xl, torch.float32, "lse")
     if splits > 1:
         check_partials(w, splits, ws, causal=causal)
