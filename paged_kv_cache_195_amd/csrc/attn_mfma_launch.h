@@ -59,6 +59,9 @@ hipError_t launch_attn_prefill_dp(const AttnParams& p, const AttnPlan& plan, int
       plan.heads_per_wg != 1)
     return hipErrorInvalidValue;
   const dim3 grid(plan.num_splits * plan.row_groups, p.num_kv_heads, batch);
+  // the kernels' workgroup order is computed in 32-bit arithmetic
+  if (static_cast<uint64_t>(grid.x) * grid.y * grid.z > 0xFFFFFFFFull)
+    return hipErrorInvalidConfiguration;
   if constexpr (kWaves == kPrefillTeamWaves) {
     static_assert(kPrefillRowBlocks == 2, "the two-team kernel holds two row blocks per wave");
     attn_prefill_pp_kernel<T, D, PS><<<grid, dim3(kWaves * 64), 0, stream>>>(p);

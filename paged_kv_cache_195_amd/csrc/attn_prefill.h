@@ -130,22 +130,22 @@ __device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem
   // L2 instead of being fetched by all eight (B=4, Sq=L=1024: 102 -> 78 us;
   // B=1, Sq=L=4096: 436 -> 376 us).  The renumbering is a bijection for any
   // grid size; the XCD count only tunes locality and order.
-  constexpr uint64_t kXcds = 8;
-  const uint64_t gx = gridDim.x, gy = gridDim.y;
-  const uint64_t n_wg = gx * gy * gridDim.z;
-  const uint64_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-  const uint64_t xcd = lin % kXcds;
-  const uint64_t per_xcd = n_wg / kXcds, extra = n_wg % kXcds;
-  const uint64_t x_first =
+  constexpr uint32_t kXcds = 8;
+  const uint32_t gx = gridDim.x, gy = gridDim.y;
+  const uint32_t n_wg = gx * gy * gridDim.z;
+  const uint32_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint32_t xcd = lin % kXcds;
+  const uint32_t per_xcd = n_wg / kXcds, extra = n_wg % kXcds;
+  const uint32_t x_first =
       xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd;
-  const uint64_t j = lin / kXcds;  // this workgroup's place in its XCD's dispatch order
-  uint64_t logical = x_first + j;
+  const uint32_t j = lin / kXcds;  // this workgroup's place in its XCD's dispatch order
+  uint32_t logical = x_first + j;
   if (extra == 0 && per_xcd % gx == 0) {
     // the XCD's range holds whole (kv head, sequence) pairs: dispatch it row
     // group by row group across its pairs, heaviest row groups first, so no
     // pair's heavy groups wait behind another pair's light ones (B=4,
     // Sq=L=1024: 75 -> 63 us; B=16: 256 -> 231 us)
-    const uint64_t pairs = per_xcd / gx;
+    const uint32_t pairs = per_xcd / gx;
     logical = x_first + (j % pairs) * gx + j / pairs;
   }
   const int bx = static_cast<int>(logical % gx);

@@ -81,18 +81,18 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 
   // XCD-aware order, as in the single-team kernel: XCD x runs a contiguous
   // range of (row group, kv head, sequence), heaviest row groups first.
-  constexpr uint64_t kXcds = 8;
-  const uint64_t gx = gridDim.x, gy = gridDim.y;
-  const uint64_t n_wg = gx * gy * gridDim.z;
-  const uint64_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-  const uint64_t xcd = lin % kXcds;
-  const uint64_t per_xcd = n_wg / kXcds, extra = n_wg % kXcds;
-  const uint64_t x_first =
+  constexpr uint32_t kXcds = 8;
+  const uint32_t gx = gridDim.x, gy = gridDim.y;
+  const uint32_t n_wg = gx * gy * gridDim.z;
+  const uint32_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint32_t xcd = lin % kXcds;
+  const uint32_t per_xcd = n_wg / kXcds, extra = n_wg % kXcds;
+  const uint32_t x_first =
       xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd;
-  const uint64_t j = lin / kXcds;
-  uint64_t logical = x_first + j;
+  const uint32_t j = lin / kXcds;
+  uint32_t logical = x_first + j;
   if (extra == 0 && per_xcd % gx == 0) {
-    const uint64_t pairs = per_xcd / gx;
+    const uint32_t pairs = per_xcd / gx;
     logical = x_first + (j % pairs) * gx + j / pairs;
   }
   const int bx = static_cast<int>(logical % gx);
