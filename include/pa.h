@@ -44,8 +44,10 @@
  *  - Device-side preconditions (the caller's contract, not checked):
  *      0 <= seq_lens[b] <= W * page_size, and
  *      0 <= block_table[b][s] < num_pages for s < ceil(seq_lens[b] / page_size).
- *    Slots at or past ceil(seq_lens[b] / page_size) are never read and may
- *    hold anything (e.g. an unmapped id such as 0x7FFFFFFF).  Token slots of a
+ *    Slots at or past ceil(seq_lens[b] / page_size) may hold anything (e.g.
+ *    an unmapped id such as 0x7FFFFFFF): no page is ever read through them
+ *    (a kernel may read such a slot's value ahead of the sequence length, but
+ *    only inside the row's W slots, and then discards it).  Token slots of a
  *    last page past seq_lens[b] are never used, even if they hold NaN.
  *  - A row with no valid key (seq_lens[b] == 0, or a causal row placed before
  *    the first key) gets out = 0 and lse = -inf.

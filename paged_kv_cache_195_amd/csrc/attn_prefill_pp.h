@@ -109,32 +109,28 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   const int Sq = p.seq_q;
   const int Hq = p.num_q_heads;
 
-  const int seq_len = p.seq_lens[b];
-  const int n_pages = (seq_len + PS - 1) / PS;
-  const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
-
-  auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
-    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
-  };
+  PageTable pt;
+  pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  // With one split the prologue's rows of this wave (tile 0, and tile 1 for
+  // team 1; see the loads below) sit in fixed slots: their ids are read
+  // beside the sequence length instead of after it.
+  const uint32_t early_id0 =
+      pt.id_early((32 * team + 8 * wt) / PS, p.table_width, p.seq_lens + b);
+  const uint32_t early_id1 =
+      pt.id_early((64 + 32 * team + 8 * wt) / PS, p.table_width, p.seq_lens + b);
   // rows of the workgroup: [wg_first, +256); team 0 owns the first 128
   const int wg_first = rg * kRowsPerWaveQ * NW;
-  const int wg_last = min(wg_first + kRowsPerWaveQ * NW, p.rows_per_kvh) - 1;
-  const int wg_max_lim = row_limit(wg_last);
   const int wave_first = wg_first + kRowsPerWaveQ * (4 * team + wt);
-  const int wave_last = min(wave_first + kRowsPerWaveQ - 1, p.rows_per_kvh - 1);
-  const int wave_min_lim = row_limit(min(wave_first, p.rows_per_kvh - 1));
-  const int wave_max_lim = wave_first < p.rows_per_kvh ? row_limit(wave_last) : 0;
-  int my_lim[RB];
+  // Q^T as the B operand, loaded first: nothing here waits for the
+  // sequence length
   u32x4 qb[RB][kKSteps];
   const float c = __builtin_fmaxf(__builtin_fabsf(p.scale_log2), 1.17549435e-38f);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wave_first + 16 * rb + li;
-    const bool valid = r < p.rows_per_kvh;
-    my_lim[rb] = valid ? row_limit(r) : 0;
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qb[rb][s] = u32x4{0u, 0u, 0u, 0u};
-    if (valid) {
+    if (r < p.rows_per_kvh) {
       const int i = r / G;
       const int h = kvh * G + (r - i * G);
       const T* qrow = static_cast<const T*>(p.q) + (static_cast<int64_t>(b * Sq + i) * Hq + h) * D;
@@ -142,12 +138,17 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
       for (int s = 0; s < kKSteps; ++s)
         qb[rb][s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
     }
-    if (p.scale_log2 < 0.f) {
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        qb[rb][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-    }
   }
+
+  const int seq_len = p.seq_lens[b];
+  const int n_pages = (seq_len + PS - 1) / PS;
+  const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
+
+  auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
+    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
+  };
+  const int wg_last = min(wg_first + kRowsPerWaveQ * NW, p.rows_per_kvh) - 1;
+  const int wg_max_lim = row_limit(wg_last);
 
   // ---- split range in pages, cut at the last page the workgroup can see
   const int per = (n_pages + S - 1) / S;
@@ -158,8 +159,6 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   const int tok_end = min(end * PS, seq_len);
   const int n_tiles = tok_end > tok_begin ? (tok_end - tok_begin + kTile - 1) / kTile : 0;
 
-  PageTable pt;
-  pt.row = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
   pt.page_bytes = static_cast<int64_t>(PS) * Hkv * kRowBytes;
   pt.n_pages = n_pages;
 
@@ -183,10 +182,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   // vr.  Lane l fills LDS position lc of row lr of each wave load (its place
   // is fixed by the lane index), so it fetches the chunk the swizzle puts there.
   typedef u32x4 VRegs[kLoads];
-  auto load_rows = [&](int tile_tok0, int buf, VRegs& vr) __attribute__((always_inline)) {
+  auto load_rows = [&](int tile_tok0, int buf, VRegs& vr, bool early = false,
+                       uint32_t early_id = 0) __attribute__((always_inline)) {
     const int tok = tile_tok0 + row0;
     if (tok < tok_end) {                                     // wave-uniform
-      const int64_t base = pt.base(tok / PS);
+      const int64_t base = early ? pt.base_of(early_id) : pt.base(tok / PS);
       const int in_page = tok % PS;
 #pragma unroll
       for (int jl = 0; jl < kLoads; ++jl) {
@@ -264,6 +264,25 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
       }
     }
   };
+
+  // prologue loads: tile 0 (both halves) and team 1's half of tile 1, all
+  // issued before the first store and before the rest of the set-up; with
+  // one split tok_begin is 0 and the rows' page ids were read early
+  VRegs vr, vr1;
+  if (n_tiles > 0) {
+    static_assert(kRowsPerWave == 8 && kTile == 64, "the early page-id slots");
+    load_rows(tok_begin, 0, vr, S == 1, early_id0);
+    if (team == 1 && n_tiles > 1) load_rows(tok_begin + kTile, 1, vr1, S == 1, early_id1);
+  }
+  const int wave_last = min(wave_first + kRowsPerWaveQ - 1, p.rows_per_kvh - 1);
+  const int wave_min_lim = row_limit(min(wave_first, p.rows_per_kvh - 1));
+  const int wave_max_lim = wave_first < p.rows_per_kvh ? row_limit(wave_last) : 0;
+  int my_lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wave_first + 16 * rb + li;
+    my_lim[rb] = r < p.rows_per_kvh ? row_limit(r) : 0;
+  }
 
   float ref[RB], msub[RB];
   f32x4 o[RB][kNBlocks];
@@ -502,15 +521,16 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   reset();
   Scores x;
   Weights pw;
-  VRegs vr;
-  // prologue: tile 0 (both halves) and team 1's half of tile 1
+  if (p.scale_log2 < 0.f) {  // a negative scale flips the scores' sign through Q
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        qb[rb][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
   if (n_tiles > 0) {
-    load_rows(tok_begin, 0, vr);
     store_v(f16v, tok_begin, 0, vr);
-    if (team == 1 && n_tiles > 1) {
-      load_rows(tok_begin + kTile, 1, vr);
-      store_v(f16v, tok_begin + kTile, 1, vr);
-    }
+    if (team == 1 && n_tiles > 1) store_v(f16v, tok_begin + kTile, 1, vr1);
   }
   __syncthreads();
   if (team == 1) __syncthreads();  // team 1 runs one phase behind

@@ -242,6 +242,7 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
         align_up(rows * static_cast<size_t>(plan.num_splits) * s->head_dim_v * sizeof(float)));
   }
   p.bt_stride = s->block_table_stride;
+  p.table_width = s->max_pages_per_seq;
   p.seq_q = s->seq_q;
   p.num_q_heads = s->num_q_heads;
   p.num_kv_heads = s->num_kv_heads;

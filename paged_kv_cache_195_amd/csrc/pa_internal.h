@@ -25,6 +25,7 @@ struct AttnParams {
   float* part_out;             // [B*Sq*Hq, S, Dv]           (num_splits > 1)
   float* part_lse;             // [B*Sq*Hq, S]               (num_splits > 1)
   int64_t bt_stride;
+  int32_t table_width;         // W: slots of each block-table row (>= every sequence's page count)
   int32_t seq_q;
   int32_t num_q_heads;
   int32_t num_kv_heads;

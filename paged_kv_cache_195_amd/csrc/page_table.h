@@ -37,6 +37,18 @@ struct PageTable {
     typedef __attribute__((address_space(4))) const int32_t* const_ptr;
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(((const_ptr)row)[slot]));
   }
+  // Physical page id in slot `slot` read before the sequence's page count is
+  // known, so that the read does not wait for the sequence length.  The
+  // read stays inside the row's `width` slots (a table with no slots reads
+  // `fallback`, any valid int32); its value may be anything unless the
+  // caller later finds slot < n_pages, which alone makes it a page id.  For
+  // a read at a kernel's start, before anything it issues may write memory:
+  // an ordinary load, which the compiler makes a scalar one there and, unlike
+  // a read of constant memory, does not repeat where the value is used.
+  __device__ __forceinline__ uint32_t id_early(int slot, int width, const int32_t* fallback) const {
+    const int32_t* src = width > 0 ? row + (slot < width ? slot : width - 1) : fallback;
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*src));
+  }
   // Byte offset of page `page_id` from the start of the cache.
   __device__ __forceinline__ int64_t base_of(uint32_t page_id) const {
     return static_cast<int64_t>(static_cast<uint64_t>(page_id)) * page_bytes;
