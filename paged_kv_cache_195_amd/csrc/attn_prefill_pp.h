@@ -131,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qb[rb][s] = u32x4{0u, 0u, 0u, 0u};
     if (r < p.rows_per_kvh) {
-      const int i = r / G;
+      const int i = div_by(r, p.group_div);
       const int h = kvh * G + (r - i * G);
       const T* qrow = static_cast<const T*>(p.q) + (static_cast<int64_t>(b * Sq + i) * Hq + h) * D;
 #pragma unroll
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
   const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
 
   auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
-    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
+    return p.causal ? causal_key_limit(seq_len, pos0, div_by(r_lin, p.group_div)) : seq_len;
   };
   const int wg_last = min(wg_first + kRowsPerWaveQ * NW, p.rows_per_kvh) - 1;
   const int wg_max_lim = row_limit(wg_last);
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const float inv_row = any ? 1.f / lsum[rb] : 0.f;
     const float lse_row = any ? (ref[rb] + log2f(lsum[rb])) * kLn2 : kNegInf;
     auto row_id = [&](int r_lin) __attribute__((always_inline)) {
-      const int i = r_lin / G;
+      const int i = div_by(r_lin, p.group_div);
       return (b * Sq + i) * Hq + kvh * G + (r_lin - i * G);
     };
     {

@@ -247,6 +247,7 @@ int run_attention(const pa_shape* s, const pa_options* opt, bool decode, const v
   p.num_q_heads = s->num_q_heads;
   p.num_kv_heads = s->num_kv_heads;
   p.group = group;
+  p.group_div = pa::div_magic(static_cast<uint32_t>(group));
   p.rows_per_kvh = s->seq_q * group;
   p.num_splits = plan.num_splits;
   p.causal = (causal != 0 || prefix_offset != nullptr) ? 1 : 0;

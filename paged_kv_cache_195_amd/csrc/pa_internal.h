@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fast_div.h"
 #include "pa.h"
 
 namespace pa {
@@ -30,6 +31,7 @@ struct AttnParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;               // Hq / Hkv
+  DivMagic group_div;          // division by group as a multiply-high (fast_div.h)
   int32_t rows_per_kvh;        // Sq * group: query rows that share one kv head
   int32_t num_splits;          // S >= 1
   int32_t causal;              // 1 also when prefix_offset is set (prefix-causal is causal)

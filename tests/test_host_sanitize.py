@@ -35,3 +35,18 @@ def test_host_layer_under_asan_and_ubsan(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "host checks passed" in run.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_fast_div_matches_division(tmp_path):
+    """The multiply-high division by the group size (csrc/fast_div.h) against
+    plain division, built with UBSan: divisors 1..4096 and random larger
+    ones, dividends around their multiples, near 2^31 and spread below it."""
+    exe = str(tmp_path / "fast_div_check")
+    cmd = ["g++", "-std=c++17", "-O1", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+           "-I", CSRC, os.path.join(HERE, "fast_div_check.cpp"), "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "fast_div checks passed" in run.stdout
