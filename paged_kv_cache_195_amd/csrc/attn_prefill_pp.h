@@ -698,18 +698,32 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
       rid[e] = valid[e] ? row_id(r_lin) : 0;
     }
     if (S == 1) {
+      // Every row of the block exists except in a tail row group: the stores
+      // then need no per-row guard (each guard cost a branch and an address
+      // rebuild around every 2-byte store).
+      const bool all_rows = wave_first + 16 * rb + 15 < p.rows_per_kvh;  // wave-uniform
 #pragma unroll
       for (int ep = 0; ep < 2; ++ep) {
         uint16_t* d0 = reinterpret_cast<uint16_t*>(static_cast<T*>(p.out) +
-                                                   static_cast<int64_t>(rid[2 * ep]) * D);
+                                                   static_cast<int64_t>(rid[2 * ep]) * D) + li;
         uint16_t* d1 = reinterpret_cast<uint16_t*>(static_cast<T*>(p.out) +
-                                                   static_cast<int64_t>(rid[2 * ep + 1]) * D);
+                                                   static_cast<int64_t>(rid[2 * ep + 1]) * D) + li;
+        if (__builtin_expect(all_rows, 1)) {
 #pragma unroll
-        for (int nb = 0; nb < kNBlocks; ++nb) {
-          const uint32_t pk = pack2(o[rb][nb][2 * ep] * inv[2 * ep],
-                                    o[rb][nb][2 * ep + 1] * inv[2 * ep + 1]);
-          if (valid[2 * ep]) d0[16 * nb + li] = static_cast<uint16_t>(pk);
-          if (valid[2 * ep + 1]) d1[16 * nb + li] = static_cast<uint16_t>(pk >> 16);
+          for (int nb = 0; nb < kNBlocks; ++nb) {
+            const uint32_t pk = pack2(o[rb][nb][2 * ep] * inv[2 * ep],
+                                      o[rb][nb][2 * ep + 1] * inv[2 * ep + 1]);
+            d0[16 * nb] = static_cast<uint16_t>(pk);
+            d1[16 * nb] = static_cast<uint16_t>(pk >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < kNBlocks; ++nb) {
+            const uint32_t pk = pack2(o[rb][nb][2 * ep] * inv[2 * ep],
+                                      o[rb][nb][2 * ep + 1] * inv[2 * ep + 1]);
+            if (valid[2 * ep]) d0[16 * nb] = static_cast<uint16_t>(pk);
+            if (valid[2 * ep + 1]) d1[16 * nb] = static_cast<uint16_t>(pk >> 16);
+          }
         }
       }
     } else {
