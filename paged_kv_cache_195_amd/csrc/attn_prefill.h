@@ -168,7 +168,7 @@ __device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem
   const int64_t pos0 = causal_row0(p.prefix_offset, b, seq_len, Sq);
 
   auto row_limit = [&](int r_lin) __attribute__((always_inline)) {
-    return p.causal ? causal_key_limit(seq_len, pos0, r_lin / G) : seq_len;
+    return p.causal ? causal_key_limit(seq_len, pos0, div_by(r_lin, p.group_div)) : seq_len;
   };
   // rows of the workgroup: [wg_first, +16 RB NW); the last one sees the most keys
   const int wg_first = rg * kRowsPerWaveQ * NW;
@@ -190,7 +190,7 @@ __device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qb[rb][s] = u32x4{0u, 0u, 0u, 0u};
     if (valid) {
-      const int i = r / G;
+      const int i = div_by(r, p.group_div);
       const int h = kvh * G + (r - i * G);
       const T* qrow = static_cast<const T*>(p.q) + (static_cast<int64_t>(b * Sq + i) * Hq + h) * D;
 #pragma unroll
@@ -756,7 +756,7 @@ __device__ __forceinline__ bool prefill_body(const AttnParams& p, lds_char* smem
           float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, ref[rb])));
       const int r_lin = wave_first + 16 * rb + 4 * g + e;
       if (r_lin >= p.rows_per_kvh) continue;
-      const int i = r_lin / G;
+      const int i = div_by(r_lin, p.group_div);
       const int rid = (b * Sq + i) * Hq + kvh * G + (r_lin - i * G);
       const bool any = le > 0.f;  // no valid key: (0, -inf) instead of 0/0
       const float lse = any ? (re + log2f(le)) * kLn2 : kNegInf;
