@@ -470,6 +470,26 @@ def test_prefill_two_team_tile_counts(dtype, causal, seq_q, splits):
         check_partials(w, splits, ws, causal=causal)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ps", [16, 32])
+def test_prefill_two_team_narrow_table(dtype, ps):
+    """With one split the two-team kernel reads the page ids of its first two
+    tiles' rows (slots up to 7 at page 16) before the sequence length, each
+    read kept inside the row's W table slots.  Here W is 4 (page 16) or 2
+    (page 32), below the slots those reads name, the sequences hold 0 to 4
+    pages, and the slots past each sequence's pages hold an unmapped id: the
+    clamped reads must stay inside the table and their values must go
+    unused."""
+    lens = [0, 1, 17, 40, 64] if ps == 16 else [0, 1, 33, 64]
+    say(f"prefill two-team narrow table {dtype} D=128 page={ps} lens={lens}")
+    w = make_custom(dtype, lens, 8, 2, 128, ps, seq_q=64, causal=True, seed=27, device=DEV)
+    assert w.block_table.shape[1] == (64 + ps - 1) // ps
+    out, lse = run(w, 1, causal=True)
+    xo, xl = oracle_full(w, causal=True)
+    assert_close(out, xo, {"f16": torch.float16, "bf16": torch.bfloat16}[dtype], "out")
+    assert_close(lse, xl, torch.float32, "lse")
+
+
 @pytest.mark.parametrize("d,ps", [(128, 16), (64, 32)])
 @pytest.mark.parametrize("splits", [1, 3])
 def test_prefill_bf16_v_beyond_f16_range(d, ps, splits):
