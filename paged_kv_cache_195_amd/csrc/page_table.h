@@ -12,9 +12,12 @@
 //  * the base is the zero-extended id times the page's byte size, formed in
 //    64-bit arithmetic, so a cache of any size up to 2^63 bytes is addressed
 //    correctly (the page above shows sign extension failing past 2^31 bytes);
-//  * only slots below the sequence's own page count are ever read, a stricter
-//    bound than one over the whole table, so an unmapped id in a slot past the
-//    sequence (or in the table's tail) is never dereferenced.
+//  * only ids of slots below the sequence's own page count ever select a
+//    page, a stricter bound than one over the whole table, so an unmapped id
+//    in a slot past the sequence (or in the table's tail) is never
+//    dereferenced (id_early below reads a slot ahead of that check, inside
+//    the row's W slots, and its caller drops the value unless the slot is
+//    mapped).
 // In-page offsets stay 32-bit: a page is far below 4 GiB.
 #pragma once
 
